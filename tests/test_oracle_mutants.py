@@ -1,0 +1,103 @@
+"""Planted mistakes in copies of the oracle must be caught by its pins (CPU only).
+
+Each mutant is the oracle's own source with one plausible slip (a dropped term,
+a wrong sign, an off-by-one mask, a transposed operand, a wrong head mapping),
+executed as a fresh module.  The real oracle is never modified.  The test
+passes when at least one pin rejects every mutant.
+"""
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _load(fname, old=None, new=None):
+    with open(os.path.join(ROOT, "oracle", fname)) as f:
+        src = f.read()
+    if old is not None:
+        assert src.count(old) >= 1, f"mutation anchor not found in {fname}: {old!r}"
+        src = src.replace(old, new, 1)
+    mod = types.ModuleType("oracle_mutant_" + fname[:-3])
+    exec(compile(src, fname, "exec"), mod.__dict__)
+    return mod
+
+
+def _pins_hold(dense, tiled):
+    """A compact subset of the pins; False as soon as one of them fails."""
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, S, D = 1, 4, 2, 19, 4
+    q = rng.standard_normal((B, Hq, S, D)) * 2
+    k = rng.standard_normal((B, Hkv, S, D))
+    v = rng.standard_normal((B, Hkv, S, D))
+    do = rng.standard_normal((B, Hq, S, D))
+    scale = 0.6
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale, enable_gqa=True)
+    out.backward(torch.tensor(do))
+    ref = {"o": out.detach().numpy(), "dq": tq.grad.numpy(), "dk": tk.grad.numpy(), "dv": tv.grad.numpy()}
+    try:
+        with np.errstate(all="ignore"):
+            g = dense.sdpa_backward(q, k, v, do, scale, True)
+            Od, Ld = dense.sdpa_forward(q, k, v, scale, True, row_block=7)
+            Or, Lr = dense.sdpa_forward_rows(q, k, v, scale, True, 0, 3, np.arange(S))
+            dqr = dense.sdpa_dq_rows(q, k, v, do, scale, True, 0, 3, np.arange(S))
+            O, L = tiled.online_forward(q, k, v, scale, True, 5, 3)
+            dq, dk, dv = tiled.online_backward(q, k, v, O, L, do, scale, True, 5, 3)
+    except Exception:
+        return False
+    ok = all(np.allclose(g[n], ref[n], atol=1e-10) for n in ref)
+    ok &= np.allclose(Od, ref["o"], atol=1e-10) and np.allclose(Ld, g["lse"], atol=1e-10)
+    ok &= np.allclose(Or, ref["o"][0, 3], atol=1e-10) and np.allclose(Lr, g["lse"][0, 3], atol=1e-10)
+    ok &= np.allclose(dqr, ref["dq"][0, 3], atol=1e-10)
+    ok &= np.allclose(O, ref["o"], atol=1e-10) and np.allclose(L, g["lse"], atol=1e-10)
+    ok &= all(np.allclose(a, ref[n], atol=1e-10) for a, n in zip((dq, dk, dv), ("dq", "dk", "dv")))
+    return bool(ok)
+
+
+def test_unmutated_oracle_passes():
+    assert _pins_hold(_load("dense.py"), _load("tiled.py"))
+
+
+DENSE_MUTANTS = [
+    ("sc = scale * (q_rows @ k_head[:ncols].T)", "sc = (q_rows @ k_head[:ncols].T)"),
+    ("> rows[:, None], -np.inf", ">= rows[:, None], -np.inf"),
+    ("e = np.exp(sc - m)", "e = np.exp(sc)"),
+    ("(m + np.log(z))[:, 0]", "(np.log(z))[:, 0]"),
+    ("dP - (P * dP).sum(axis=1, keepdims=True)", "dP + (P * dP).sum(axis=1, keepdims=True)"),
+    ("dP = do_blk @ vh[:nc].T", "dP = do_blk @ vh[:nc].T * 0.5"),
+    ('out["dq"][b, h, r0:r1] = scale * (dS @ kh[:nc])', 'out["dq"][b, h, r0:r1] = (dS @ kh[:nc])'),
+    ("dk[:nc] += scale * (dS.T @ qh[r0:r1])", "dk[:nc] += scale * (P.T @ qh[r0:r1])"),
+    ("dv[:nc] += P.T @ _f64(do[b, h, r0:r1])", "dv[:nc] += dS.T @ _f64(do[b, h, r0:r1])"),
+    ("return h // (Hq // Hkv)", "return h % Hkv"),
+]
+
+TILED_MUTANTS = [
+    ("ell = ell * alpha + p.sum(axis=1)", "ell = ell + p.sum(axis=1)"),
+    ("acc = acc * alpha[:, None] + p @ Vh[j0:j1]", "acc = acc + p @ Vh[j0:j1]"),
+    ("if causal and j0 > i1 - 1:", "if causal and j0 > i0:"),
+    ("L[b, h, i0:i1] = m + np.log(ell)", "L[b, h, i0:i1] = np.log(ell)"),
+    ("bad = bad | (k_pos[None, :] > q_pos[:, None])", "bad = bad | (k_pos[None, :] >= q_pos[:, None])"),
+    ("np.exp(s - lse[b, h, i0:i1, None])", "np.exp(s - 0 * lse[b, h, i0:i1, None])"),
+    ("ds = p * (dp - Dvec[b, h, i0:i1, None])", "ds = p * (dp + Dvec[b, h, i0:i1, None])"),
+    ("dQ[b, h, i0:i1] += scale * (ds @ Kj)", "dQ[b, h, i0:i1] += scale * (p @ Kj)"),
+    ("dKj += scale * (ds.T @ Qi)", "dKj += (ds.T @ Qi)"),
+    ("first = (j0 // br) * br if causal else 0", "first = (j0 // br + 1) * br if causal else 0"),
+    ("Dvec = (do * o).sum(axis=-1)", "Dvec = (do * o).sum(axis=-1) * 0"),
+    ("g = h // G\n            Kh, Vh", "g = h % Hkv\n            Kh, Vh"),
+]
+
+
+@pytest.mark.parametrize("old,new", DENSE_MUTANTS)
+def test_dense_mutant_is_caught(old, new):
+    assert not _pins_hold(_load("dense.py", old, new), _load("tiled.py"))
+
+
+@pytest.mark.parametrize("old,new", TILED_MUTANTS)
+def test_tiled_mutant_is_caught(old, new):
+    assert not _pins_hold(_load("dense.py"), _load("tiled.py", old, new))

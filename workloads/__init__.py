@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module is shared by the tests, the benchmark and the CPU oracle's callers.
+It holds no attention arithmetic: it only names the workload shapes and draws
+and rounds random tensors.  Both the HIP path and the oracle consume the exact
+same rounded values, so any difference between them comes from the method,
+never from the inputs.
+
+Shapes follow the pages' workloads: GPT-2-small heads (12 x 64) and Qwen3-style
+GQA (32 query heads over 8 KV heads, head dim 128) from "Phase 14: Flash
+Attention 2 for SM120" (kernel configuration and GQA sections), the
+[1, 8, 4096, 64] fp16 causal tensor of "FlashAttention 与 SDPA Backend"
+(memory and IO section) and of the udemi.tech "Flash Attention" usage snippet.
+
+Recipe (per workload): ``rng = numpy.random.default_rng(seed)``; draw q, k, v
+and then dO (when the workload has a backward pass), each as a float32
+``standard_normal`` of its full shape; q is multiplied by ``q_std``; each tensor
+is then rounded to the workload dtype with round-to-nearest-even.  The rounded
+values are returned as float32 arrays, which hold bf16 / fp16 values exactly.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    S: int
+    D: int
+    seed: int
+    q_std: float = 1.0
+    backward: bool = True
+    causal: bool = True
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    def causal_pairs(self) -> int:
+        """(query, key) pairs the causal method must visit, over all heads."""
+        per_head = self.S * (self.S + 1) // 2 if self.causal else self.S * self.S
+        return self.B * self.Hq * per_head
+
+    def fwd_flops(self) -> float:
+        # QK^T and PV: 2 * D flops each per visited pair.
+        return 4.0 * self.D * self.causal_pairs()
+
+    def bwd_flops(self) -> float:
+        # five products per visited pair (S recompute, dP, dV, dK, dQ).
+        return 10.0 * self.D * self.causal_pairs()
+
+
+# The five workloads, named by what they are.
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("causal_f32_b1_h2_s128_d64", "f32", 1, 2, 2, 128, 64, seed=0),
+        Workload("gpt2s_causal_bf16_b8_h12_s1024_d64", "bf16", 8, 12, 12, 1024, 64, seed=1),
+        Workload("qwen3_gqa_causal_bf16_b4_h32kv8_s2048_d128", "bf16", 4, 32, 8, 2048, 128,
+                 seed=2, backward=False),
+        Workload("causal_f16_b1_h8_s4096_d64", "f16", 1, 8, 8, 4096, 64, seed=3),
+        Workload("longctx_gqa_causal_bf16_b1_h32kv8_s16384_d128", "bf16", 1, 32, 8, 16384, 128,
+                 seed=4, q_std=3.0),
+    )
+}
+SMALL = "causal_f32_b1_h2_s128_d64"
+LONG_CONTEXT = "longctx_gqa_causal_bf16_b1_h32kv8_s16384_d128"
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        return round_bf16(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(B, Hq, Hkv, S, D, dtype, seed, q_std=1.0, backward=True):
+    """Draw q, k, v (and dO) per the recipe above.  Returns a dict of float32 arrays."""
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
+    if q_std != 1.0:
+        q *= np.float32(q_std)
+    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    out = {"q": round_to(q, dtype), "k": round_to(k, dtype), "v": round_to(v, dtype)}
+    if backward:
+        out["do"] = round_to(rng.standard_normal((B, Hq, S, D), dtype=np.float32), dtype)
+    return out
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.seed, w.q_std, w.backward)
