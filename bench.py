@@ -1,0 +1,310 @@
+"""Benchmark: causal attention fwd + bwd through libfa.so on one MI355X.
+
+One step = fa_fwd then fa_bwd (forward kernel, row-dot kernel, dK/dV kernel,
+dQ kernel) over the long-context GQA workload (B=1, Hq=32, Hkv=8, S=16384,
+D=128, bf16, causal) with every input already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-memory]
+
+Prints one JSON line.  ``value`` is causal fwd+bwd TFLOP/s: 4*D flops per
+visited (query, key) pair for the forward and 10*D for the backward, pairs =
+B*Hq*S*(S+1)/2, divided by the measured time per step.  Per-kernel durations
+come from HIP events the library records around each of its kernel launches
+(fa_profile_events) during the same timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import LONG_CONTEXT, WORKLOADS, workload_inputs  # noqa: E402
+
+METRIC = "attention fwd+bwd TFLOP/s (causal) and % of bf16 MFMA peak at 1 MI355X"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_FP32_MATRIX_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNELS = ("fwd", "rowdot", "dkdv", "dq")
+
+
+class Hip:
+    """The few HIP runtime calls bench needs (events), via ctypes."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        vp = ctypes.c_void_p
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(vp)]
+        self.h.hipEventRecord.argtypes = [vp, vp]
+        self.h.hipEventSynchronize.argtypes = [vp]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        self.h.hipEventDestroy.argtypes = [vp]
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def event(self):
+        e = ctypes.c_void_p()
+        self._ok(self.h.hipEventCreate(ctypes.byref(e)), "hipEventCreate")
+        return e
+
+    def record(self, e, stream):
+        self._ok(self.h.hipEventRecord(e, stream), "hipEventRecord")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        self._ok(self.h.hipEventElapsedTime(ctypes.byref(out), a, b), "hipEventElapsedTime")
+        return float(out.value)
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def algorithmic_work(w):
+    """Per-kernel algorithmic work of one step (flops, or bytes for the row-dot kernel)."""
+    pairs = w.causal_pairs()
+    D = w.D
+    elem = {"bf16": 2, "f16": 2, "f32": 4}[w.dtype]
+    rows = w.B * w.Hq * w.S
+    return {
+        "fwd": 4.0 * D * pairs,            # Q K^T and P V
+        "dkdv": 8.0 * D * pairs,           # S and dP (recomputed), dV, dK
+        "dq": 2.0 * D * pairs,             # dQ (its S / dP recompute is overhead of the split)
+        "rowdot": 2.0 * rows * D * elem + 4.0 * rows,   # read O and dO, write D (bytes)
+    }
+
+
+def run_gpu(w, steps, warmup):
+    import numpy as np  # noqa: F401
+    import torch
+
+    import causal_attention_fa_amd as fa
+
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    code = {"bf16": fa.FA_BF16, "f16": fa.FA_F16, "f32": fa.FA_F32}[w.dtype]
+    inp = workload_inputs(w)
+    t = {n: torch.from_numpy(x).to(dev).to(tdt).contiguous() for n, x in inp.items()}
+    del inp
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+    hip = Hip()
+    args = (w.B, w.Hq, w.Hkv, w.S, w.D, w.scale, int(w.causal), code)
+
+    def step():
+        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), *args, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_fwd")
+        st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *args, ws.data_ptr(), ws.numel(), sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_bwd")
+
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # per step: fwd before/after (2) and bwd rowdot/dkdv/dq boundaries (4)
+    evs = [[hip.event() for _ in range(6)] for _ in range(steps)]
+    arrays = [((ctypes.c_void_p * 2)(evs[s][0].value, evs[s][1].value),
+               (ctypes.c_void_p * 4)(*[e.value for e in evs[s][2:]])) for s in range(steps)]
+    start, end = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(start, sh)
+    for s in range(steps):
+        fa.fa_profile_events(ctypes.addressof(arrays[s][0]), 2)
+        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), *args, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_fwd")
+        fa.fa_profile_events(ctypes.addressof(arrays[s][1]), 4)
+        st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *args, ws.data_ptr(), ws.numel(), sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_bwd")
+    fa.fa_profile_events(None, 0)
+    hip.record(end, sh)
+    torch.cuda.synchronize()
+    total_ms = hip.ms(start, end)
+    per = {n: [] for n in KERNELS}
+    for s in range(steps):
+        e = evs[s]
+        per["fwd"].append(hip.ms(e[0], e[1]))
+        per["rowdot"].append(hip.ms(e[2], e[3]))
+        per["dkdv"].append(hip.ms(e[3], e[4]))
+        per["dq"].append(hip.ms(e[4], e[5]))
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    hip.destroy(start)
+    hip.destroy(end)
+    kernel_ms = {n: sum(x) / len(x) for n, x in per.items()}
+    del t, q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return total_ms / steps, kernel_ms
+
+
+def peak_memory(w):
+    """Peak device memory of fa fwd+bwd above the inputs, vs materialised [B,Hq,S,S] scores
+    (allocator protocol: baseline after inputs, reset peak, run, read peak)."""
+    import torch
+
+    import causal_attention_fa_amd as fa
+
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    elem = {"bf16": 2, "f16": 2, "f32": 4}[w.dtype]
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    q = torch.randn((w.B, w.Hq, w.S, w.D), device=dev, dtype=tdt, generator=g)
+    k = torch.randn((w.B, w.Hkv, w.S, w.D), device=dev, dtype=tdt, generator=g)
+    v = torch.randn((w.B, w.Hkv, w.S, w.D), device=dev, dtype=tdt, generator=g)
+    do = torch.randn((w.B, w.Hq, w.S, w.D), device=dev, dtype=tdt, generator=g)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    o, lse = fa.forward(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev)
+    live = sum(x.numel() * x.element_size() for x in (o, lse, dq, dk, dv))
+    scores = w.B * w.Hq * w.S * w.S * elem
+    out = {
+        "workload": w.name,
+        "baseline_MiB": round(base / 2**20, 2),
+        "peak_MiB": round(peak / 2**20, 2),
+        "above_baseline_MiB": round((peak - base) / 2**20, 2),
+        "live_outputs_MiB": round(live / 2**20, 2),
+        "bwd_workspace_MiB": round(fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D) / 2**20, 2),
+        "materialised_scores_one_matrix_MiB": round(scores / 2**20, 2),
+        "materialised_fwd_bwd_MiB": round(4 * scores / 2**20, 2),
+        "note": "materialised baseline = [B,Hq,S,S] in dtype per matrix; fwd keeps scores and probs, "
+                "bwd adds dP and dS (4 matrices); fa keeps O(S*D) outputs plus an fp32 [B*Hq*S] workspace",
+    }
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w):
+    """The fp64 oracle (dense form) timed on the host on one whole KV group of the workload."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                      default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    inp = workload_inputs(w)
+    G = w.group
+    sl = {"q": inp["q"][:1, :G], "k": inp["k"][:1, :1], "v": inp["v"][:1, :1], "do": inp["do"][:1, :G]}
+    t0 = time.perf_counter()
+    oracle.sdpa_backward(sl["q"], sl["k"], sl["v"], sl["do"], w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    per_head = w.S * (w.S + 1) // 2 if w.causal else w.S * w.S
+    flops = 14.0 * w.D * per_head * G
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"dense fp64 oracle fwd+bwd of one KV group (batch 0, KV head 0, its {G} query heads, "
+                  f"all {w.S} rows) = {flops:.3e} causal flops in {dt:.1f} s; same flop count as the GPU line",
+        "seconds": round(dt, 2),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=LONG_CONTEXT, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-memory", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
+              f"multi-GPU path; the attention shards by (batch, KV head) with no communication.",
+              file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    if not w.backward:
+        raise SystemExit(f"{w.name} is a forward-only workload; bench times fwd+bwd")
+
+    ms_step, kms = run_gpu(w, args.steps, args.warmup)
+    work = algorithmic_work(w)
+    flops_step = w.fwd_flops() + w.bwd_flops()
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    peak = PEAK_FP32_MATRIX_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+
+    kernels = {}
+    for n in KERNELS:
+        t_s = kms[n] * 1e-3
+        if n == "rowdot":
+            a = work[n] / t_s / 1e9
+            kernels[n] = {"ms": round(kms[n], 4), "bound": "hbm", "achieved": round(a, 1), "unit": "GB/s",
+                          "frac": round(a / PEAK_HBM_GBS, 4)}
+        else:
+            a = work[n] / t_s / 1e12
+            kernels[n] = {"ms": round(kms[n], 4), "bound": "mfma", "achieved": round(a, 1), "unit": "TFLOP/s",
+                          "frac": round(a / peak, 4)}
+    dom = max(KERNELS, key=lambda n: kms[n])
+    kd = kernels[dom]
+    roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"],
+                "peak": PEAK_HBM_GBS if kd["bound"] == "hbm" else peak, "unit": kd["unit"], "frac": kd["frac"],
+                "traffic": None,
+                "work_per_launch": work[dom],
+                "work_note": "fwd 4*D, dkdv 8*D, dq 2*D flops per visited causal pair; rowdot bytes = read O, dO "
+                             "+ write D"}
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+                   "causal": w.causal, "scale": w.scale, "flops_per_step": flops_step},
+        "pct_of_bf16_peak": round(100.0 * tflops / peak, 2),
+        "forward": {"ms": round(kms["fwd"], 4), "tflops": kernels["fwd"]["achieved"],
+                    "pct_of_bf16_peak": round(100.0 * kernels["fwd"]["frac"], 2)},
+        "backward": {"ms": round(kms["rowdot"] + kms["dkdv"] + kms["dq"], 4),
+                     "tflops": round(w.bwd_flops() / ((kms["rowdot"] + kms["dkdv"] + kms["dq"]) * 1e-3) / 1e12, 1)},
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_memory:
+        out["memory"] = [peak_memory(w), peak_memory(WORKLOADS["causal_f16_b1_h8_s4096_d64"])]
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

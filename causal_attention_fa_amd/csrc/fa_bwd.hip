@@ -1,0 +1,382 @@
+// fa_bwd.hip -- backward pass of softmax attention, recomputing P from Q, K and L.
+//
+// Method: "Phase T14: 融合 Flash-Attention Kernel — Design Document", section
+// "什么是 flash-attention" (recompute s = scale Q K^T, p = exp(s - L),
+// dp = dO V^T, ds = p (dp - D) scale, then dQ += ds K, dK += ds^T Q,
+// dV += p^T dO) and decision ③ (D[i] = sum_d dO[i,d] O[i,d] replaces the
+// softmax Jacobian).  GQA head mapping from "Phase 14: Flash Attention 2 for
+// SM120 — Design Document", section "GQA 支持"; dK and dV of a KV head are the
+// sums over the query heads of its group.
+//
+// Three kernels on the caller's stream:
+//   rowdot_kernel  D = rowsum(dO * O) in fp32 (HBM-bound, one pass).
+//   dkdv_kernel    KV-tile outer: a workgroup owns 32*NW keys of one (b, KV
+//                  head) and keeps their dK, dV accumulators in registers while
+//                  it walks every query head of the group and every query tile
+//                  that can see those keys.  No atomics: each dK / dV row has
+//                  exactly one owner.
+//   dq_kernel      query-tile outer, shaped like the forward: a workgroup owns
+//                  32*NW query rows, keeps Q, dO, L and D of its rows in
+//                  registers and walks the KV tiles.  dQ rows have one owner,
+//                  so dQ needs no fp32 atomics either.
+// The split recomputes S and dP in both kernels (7 products per (q, k) pair
+// instead of 5) in exchange for no atomic traffic and deterministic outputs.
+//
+// Layout choices (MI355X-specific):
+//   dkdv: S = Q K^T and dP = dO V^T are formed with the wave's keys as MFMA
+//   columns, so P and dS come out of the accumulators as the B operands of
+//   dV^T += dO^T P and dK^T += Q^T dS.  Q and dO tiles are staged in LDS both
+//   row-major (A operands of S and dP) and transposed (A operands of the
+//   gradient products).  L and D of the tile's rows are staged in LDS too.
+//   dq: S^T = K Q^T and dP^T = V dO^T put one query row per lane pair (like
+//   the forward), and dS^T is the B operand of dQ^T += K^T dS^T; K is staged
+//   row-major and transposed, V row-major.
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+// ------------------------------------------------------------------ D = rowsum(dO * O)
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, const T* __restrict__ dO,
+                                                     float* __restrict__ Dd, long long rows) {
+  constexpr int kEpv = Elem<T>::kEpv;
+  constexpr int kLanesPerRow = HD / kEpv;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int col = (threadIdx.x % kLanesPerRow) * kEpv;
+  float acc = 0.f;
+  if (row < rows) {
+    Unit<T> a = load_unit<T>(O + row * HD + col);
+    Unit<T> b = load_unit<T>(dO + row * HD + col);
+    const T* ea = reinterpret_cast<const T*>(&a.bits);
+    const T* eb = reinterpret_cast<const T*>(&b.bits);
+#pragma unroll
+    for (int e = 0; e < kEpv; ++e) acc = fmaf((float)ea[e], (float)eb[e], acc);
+  }
+#pragma unroll
+  for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && threadIdx.x % kLanesPerRow == 0) Dd[row] = acc;
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <typename T, int HD, int BQ, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dK, T* __restrict__ dV,
+    int Hq, int Hkv, int S, float c, float scale) {
+  constexpr int BKV = 32 * NW;
+  constexpr int NT = NW * 64;
+  using QRow = RowTile<T, BQ, HD>;
+  using QTr = TrTile<T, HD, BQ>;
+  constexpr int kOffQr = 0;
+  constexpr int kOffDr = QRow::kElems;
+  constexpr int kOffQt = 2 * QRow::kElems;
+  constexpr int kOffDt = 2 * QRow::kElems + QTr::kElems;
+  constexpr int kElems = 2 * QRow::kElems + 2 * QTr::kElems;
+  __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
+  __shared__ __attribute__((aligned(16))) float lds_ld[2][2][BQ];  // [buf][L*log2e, D][row]
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int kvt = blockIdx.x;  // small key tiles see the most queries: launched first
+  const int bg = blockIdx.y;   // b * Hkv + hkv
+  const int b = bg / Hkv, hkv = bg - b * Hkv;
+  const int G = Hq / Hkv;
+  const int kv0 = kvt * BKV;
+  const int kw0 = kv0 + 32 * w;
+  const int mykv = kw0 + r;
+  const T* Kh = K + (size_t)bg * S * HD;
+  const T* Vh = V + (size_t)bg * S * HD;
+
+  vec8<T> kf[HD / 16], vf[HD / 16];
+#pragma unroll
+  for (int t = 0; t < HD / 16; ++t) {
+    kf[t] = mykv < S ? load8<T>(Kh + (size_t)mykv * HD + 16 * t + 8 * h) : zero8<T>();
+    vf[t] = mykv < S ? load8<T>(Vh + (size_t)mykv * HD + 16 * t + 8 * h) : zero8<T>();
+  }
+  f32x16 dk[HD / 32], dv[HD / 32];
+#pragma unroll
+  for (int d = 0; d < HD / 32; ++d) {
+    dk[d] = f32x16{};
+    dv[d] = f32x16{};
+  }
+
+  const int first = CAUSAL ? (kv0 / BQ) : 0;
+  const int nqt = (S + BQ - 1) / BQ;
+  const int per_head = nqt - first;
+  const int total = G * per_head;
+
+  Stager<T, BQ, HD, NT> qst, dost;
+  float ld_l = 0.f, ld_d = 0.f;
+  auto issue = [&](int it) {
+    const int hq = hkv * G + it / per_head;
+    const int i0 = (first + it % per_head) * BQ;
+    const size_t qoff = ((size_t)b * Hq + hq) * S * HD;
+    qst.load(Q + qoff, i0, S, tid);
+    dost.load(dO + qoff, i0, S, tid);
+    if (tid < BQ) {
+      const size_t row = ((size_t)b * Hq + hq) * S + i0 + tid;
+      const bool ok = i0 + tid < S;
+      ld_l = ok ? LSE[row] * kLog2e : 0.f;
+      ld_d = ok ? Dd[row] : 0.f;
+    }
+  };
+  auto commit = [&](int buf) {
+    T* base = lds + buf * kElems;
+    qst.store_rows(base + kOffQr, tid);
+    dost.store_rows(base + kOffDr, tid);
+    qst.store_transposed(base + kOffQt, tid);
+    dost.store_transposed(base + kOffDt, tid);
+    if (tid < BQ) {
+      lds_ld[buf][0][tid] = ld_l;
+      lds_ld[buf][1][tid] = ld_d;
+    }
+  };
+
+  if (total > 0) {
+    issue(0);
+    commit(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
+    const int i0 = (first + it % per_head) * BQ;
+    const bool more = it + 1 < total;
+    if (more) issue(it + 1);
+    const T* base = lds + buf * kElems;
+    const bool active = !CAUSAL || (i0 + BQ - 1 >= kw0);
+    if (active) {
+      // S, dP (BQ x 32): rows = queries of the tile, columns = this wave's keys
+      f32x16 s[BQ / 32], dp[BQ / 32];
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb) {
+        s[qb] = f32x16{};
+        dp[qb] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t) {
+          s[qb] = mma<T>(QRow::frag(base + kOffQr, 32 * qb + r, 16 * t, h), kf[t], s[qb]);
+          dp[qb] = mma<T>(QRow::frag(base + kOffDr, 32 * qb + r, 16 * t, h), vf[t], dp[qb]);
+        }
+      }
+      const bool edge = (CAUSAL && i0 < kw0 + 31) || (i0 + BQ > S);
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int qrow = 32 * qb + 8 * g4 + 4 * h;  // first of 4 consecutive query rows
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][0][qrow]);
+          const f32x4 dvv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][1][qrow]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * g4 + e;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c, -lv[e]));
+            if (edge) {
+              const int q = i0 + qrow + e;
+              const bool masked = (CAUSAL && mykv > q) || q >= S;
+              p = masked ? 0.f : p;
+            }
+            s[qb][i] = p;
+            dp[qb][i] = p * (dp[qb][i] - dvv[e]);
+          }
+        }
+      // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over the tile's queries)
+#pragma unroll
+      for (int kt = 0; kt < BQ / 16; ++kt) {
+        const vec8<T> pf = acc_to_frag<T>(s[kt >> 1], 8 * (kt & 1));
+        const vec8<T> sf = acc_to_frag<T>(dp[kt >> 1], 8 * (kt & 1));
+#pragma unroll
+        for (int d = 0; d < HD / 32; ++d) {
+          dv[d] = mma<T>(QTr::frag(base + kOffDt, 32 * d + r, kt, h), pf, dv[d]);
+          dk[d] = mma<T>(QTr::frag(base + kOffQt, 32 * d + r, kt, h), sf, dk[d]);
+        }
+      }
+    }
+    if (more) commit(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (mykv < S) {
+    T* dKr = dK + (size_t)bg * S * HD + (size_t)mykv * HD;
+    T* dVr = dV + (size_t)bg * S * HD + (size_t)mykv * HD;
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * d + 8 * g + 4 * h;
+        store4<T>(dKr + col, dk[d][4 * g] * scale, dk[d][4 * g + 1] * scale, dk[d][4 * g + 2] * scale,
+                  dk[d][4 * g + 3] * scale);
+        store4<T>(dVr + col, dv[d][4 * g], dv[d][4 * g + 1], dv[d][4 * g + 2], dv[d][4 * g + 3]);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <typename T, int HD, int BC, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
+    const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dQ, int Hq, int Hkv, int S,
+    float c, float scale, int nqt) {
+  constexpr int BR = 32 * NW;
+  constexpr int NT = NW * 64;
+  using KRow = RowTile<T, BC, HD>;
+  using KTr = TrTile<T, HD, BC>;
+  constexpr int kOffK = 0;
+  constexpr int kOffV = KRow::kElems;
+  constexpr int kOffKt = 2 * KRow::kElems;
+  constexpr int kElems = 2 * KRow::kElems + KTr::kElems;
+  __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / Hq, hq = bh - b * Hq;
+  const int hkv = hq / (Hq / Hkv);
+  const T* Qh = Q + (size_t)bh * S * HD;
+  const T* dOh = dO + (size_t)bh * S * HD;
+  const T* Kh = K + ((size_t)b * Hkv + hkv) * S * HD;
+  const T* Vh = V + ((size_t)b * Hkv + hkv) * S * HD;
+  const int i0 = qt * BR;
+  const int qw0 = i0 + 32 * w;
+  const int myq = qw0 + r;
+
+  vec8<T> qf[HD / 16], df[HD / 16];
+#pragma unroll
+  for (int t = 0; t < HD / 16; ++t) {
+    qf[t] = myq < S ? load8<T>(Qh + (size_t)myq * HD + 16 * t + 8 * h) : zero8<T>();
+    df[t] = myq < S ? load8<T>(dOh + (size_t)myq * HD + 16 * t + 8 * h) : zero8<T>();
+  }
+  const float lq = myq < S ? LSE[(size_t)bh * S + myq] * kLog2e : 0.f;
+  const float dq_d = myq < S ? Dd[(size_t)bh * S + myq] : 0.f;
+  f32x16 acc[HD / 32];
+#pragma unroll
+  for (int d = 0; d < HD / 32; ++d) acc[d] = f32x16{};
+
+  const int kv_end = CAUSAL ? min(S, i0 + BR) : S;
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  Stager<T, BC, HD, NT> kst, vst;
+  kst.load(Kh, 0, S, tid);
+  vst.load(Vh, 0, S, tid);
+  kst.store_rows(lds + kOffK, tid);
+  kst.store_transposed(lds + kOffKt, tid);
+  vst.store_rows(lds + kOffV, tid);
+  __syncthreads();
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const int j0 = jt * BC;
+    const bool more = jt + 1 < ntiles;
+    if (more) {
+      kst.load(Kh, j0 + BC, S, tid);
+      vst.load(Vh, j0 + BC, S, tid);
+    }
+    const T* base = lds + (jt & 1) * kElems;
+    const bool active = !CAUSAL || j0 <= qw0 + 31;
+    if (active) {
+      f32x16 s[BC / 32], dp[BC / 32];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t) {
+          s[kb] = mma<T>(KRow::frag(base + kOffK, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
+          dp[kb] = mma<T>(KRow::frag(base + kOffV, 32 * kb + r, 16 * t, h), df[t], dp[kb]);
+        }
+      }
+      const bool edge = CAUSAL ? (j0 + BC - 1 > qw0) : (j0 + BC > S);
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -lq));
+          if (edge) {
+            const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+            const bool masked = CAUSAL ? (kv > myq) : (kv >= S);
+            p = masked ? 0.f : p;
+          }
+          dp[kb][i] = p * (dp[kb][i] - dq_d);
+        }
+      // dQ^T (HD x 32) += K_tile^T dS^T
+#pragma unroll
+      for (int kt = 0; kt < BC / 16; ++kt) {
+        const vec8<T> sf = acc_to_frag<T>(dp[kt >> 1], 8 * (kt & 1));
+#pragma unroll
+        for (int d = 0; d < HD / 32; ++d) acc[d] = mma<T>(KTr::frag(base + kOffKt, 32 * d + r, kt, h), sf, acc[d]);
+      }
+    }
+    if (more) {
+      T* nb = lds + ((jt + 1) & 1) * kElems;
+      kst.store_rows(nb + kOffK, tid);
+      kst.store_transposed(nb + kOffKt, tid);
+      vst.store_rows(nb + kOffV, tid);
+    }
+    __syncthreads();
+  }
+
+  if (myq < S) {
+    T* dQr = dQ + (size_t)bh * S * HD + (size_t)myq * HD;
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<T>(dQr + 32 * d + 8 * g + 4 * h, acc[d][4 * g] * scale, acc[d][4 * g + 1] * scale,
+                  acc[d][4 * g + 2] * scale, acc[d][4 * g + 3] * scale);
+  }
+}
+
+// ------------------------------------------------------------------ launch
+template <typename T, int HD, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+  const long long rows = (long long)a.B * a.Hq * a.S;
+  {
+    constexpr int kRowsPerBlock = 256 / (HD / Elem<T>::kEpv);
+    dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+    mark(a.ev, a.nev, 0, st);
+    hipLaunchKernelGGL((rowdot_kernel<T, HD>), grid, dim3(256), 0, st, (const T*)a.o, (const T*)a.dO, a.rowdot,
+                       rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const float c = a.scale * kLog2e;
+  {
+    constexpr int NW = 4, BQ = (HD == 128 || sizeof(T) == 4) ? 32 : 64;
+    const int nkt = (a.S + 32 * NW - 1) / (32 * NW);
+    dim3 grid(nkt, a.B * a.Hkv);
+    mark(a.ev, a.nev, 1, st);
+    hipLaunchKernelGGL((dkdv_kernel<T, HD, BQ, NW, CAUSAL>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dk,
+                       (T*)a.dv, a.Hq, a.Hkv, a.S, c, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    // fp32 at D=128 would need 200 KiB of LDS with 64-key tiles: use 32.
+    constexpr int NW = 4, BC = (sizeof(T) == 4 && HD == 128) ? 32 : 64;
+    const int nqt = (a.S + 32 * NW - 1) / (32 * NW);
+    dim3 grid(nqt, a.B * a.Hq);
+    mark(a.ev, a.nev, 2, st);
+    hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dq,
+                       a.Hq, a.Hkv, a.S, c, a.scale, nqt);
+    mark(a.ev, a.nev, 3, st);
+    return hipGetLastError();
+  }
+}
+
+template <typename T>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
+  if (a.D == 64) return a.causal ? launch_bwd_t<T, 64, true>(a, st) : launch_bwd_t<T, 64, false>(a, st);
+  return a.causal ? launch_bwd_t<T, 128, true>(a, st) : launch_bwd_t<T, 128, false>(a, st);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+  switch (a.dtype) {
+    case 0: return launch_bwd_d<float>(a, st);
+    case 1: return launch_bwd_d<_Float16>(a, st);
+    default: return launch_bwd_d<__bf16>(a, st);
+  }
+}
+
+}  // namespace fa

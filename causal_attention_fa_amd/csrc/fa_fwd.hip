@@ -1,0 +1,184 @@
+// fa_fwd.hip -- forward pass: O = softmax(mask(scale * Q K^T)) V and L = logsumexp,
+// by online softmax over KV tiles (gfx950, wave64, 32x32 MFMA).
+//
+// Method: "Phase 14: Flash Attention 2 for SM120 — Design Document", section
+// "FA2 算法" (Q tile outer, loaded once; KV tiles inner; running max / sum with
+// rescale by exp(m - m_new)); section "Causal Mask" (tiles wholly after the
+// diagonal are skipped, the rest masked per element); section "GQA 支持"
+// (KV head = query head / group size, indexed in the kernel).  L = m + log l is
+// the forward's saved state ("Phase T14: 融合 Flash-Attention Kernel — Design
+// Document", section "什么是 flash-attention" and decision ②).
+//
+// Work decomposition (MI355X-specific, not the pages'):
+//   * one workgroup = NW waves = one tile of 32*NW query rows of one (b, head);
+//   * each wave owns 32 query rows.  It computes S^T = K Q^T so that one query
+//     row sits in one lane pair: the softmax max is a register max plus one
+//     cross-half exchange, the rescale factor is a per-lane scalar, and the
+//     probabilities P^T come out of the accumulators already laid out as the B
+//     operand of O^T += V^T P^T (no LDS round trip for P);
+//   * Q stays in registers (B operand of S^T) for the whole kernel;
+//   * K (row-major) and V (transposed) tiles are staged in LDS, double
+//     buffered: the next tile's global loads are issued before the current
+//     tile's math and written to the other buffer after it;
+//   * softmax in base 2: p = exp2(s * scale*log2e - m), m tracked in that unit;
+//   * causal: workgroups are launched heaviest (last query tiles) first, a wave
+//     skips KV tiles that lie wholly after its rows, and the element mask is
+//     applied on diagonal tiles only.
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+template <typename T, int HD, int BC, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
+    float* __restrict__ LSE, int Hq, int Hkv, int S, float c, int nqt) {
+  constexpr int BR = 32 * NW;
+  constexpr int NT = NW * 64;
+  using KTile = RowTile<T, BC, HD>;
+  using VTile = TrTile<T, HD, BC>;
+  constexpr int kBuf = KTile::kElems + VTile::kElems;
+  __shared__ __attribute__((aligned(16))) T lds[2 * kBuf];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / Hq, hq = bh - b * Hq;
+  const int hkv = hq / (Hq / Hkv);
+  const T* Qh = Q + (size_t)bh * S * HD;
+  const T* Kh = K + ((size_t)b * Hkv + hkv) * S * HD;
+  const T* Vh = V + ((size_t)b * Hkv + hkv) * S * HD;
+  const int i0 = qt * BR;
+  const int qw0 = i0 + 32 * w;
+  const int myq = qw0 + r;
+
+  vec8<T> qf[HD / 16];
+#pragma unroll
+  for (int t = 0; t < HD / 16; ++t)
+    qf[t] = myq < S ? load8<T>(Qh + (size_t)myq * HD + 16 * t + 8 * h) : zero8<T>();
+
+  f32x16 oacc[HD / 32];
+#pragma unroll
+  for (int d = 0; d < HD / 32; ++d) oacc[d] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  const int kv_end = CAUSAL ? min(S, i0 + BR) : S;
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  Stager<T, BC, HD, NT> kst, vst;
+  kst.load(Kh, 0, S, tid);
+  vst.load(Vh, 0, S, tid);
+  kst.store_rows(lds, tid);
+  vst.store_transposed(lds + KTile::kElems, tid);
+  __syncthreads();
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const int j0 = jt * BC;
+    const bool more = jt + 1 < ntiles;
+    if (more) {
+      kst.load(Kh, j0 + BC, S, tid);
+      vst.load(Vh, j0 + BC, S, tid);
+    }
+    const T* Ks = lds + (jt & 1) * kBuf;
+    const T* Vt = Ks + KTile::kElems;
+    const bool active = !CAUSAL || j0 <= qw0 + 31;
+    if (active) {
+      // S^T (BC x 32) = K_tile Q_w^T
+      f32x16 s[BC / 32];
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t) s[kb] = mma<T>(KTile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
+      }
+      const bool edge = CAUSAL ? (j0 + BC - 1 > qw0) : (j0 + BC > S);
+      if (edge) {
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+            const bool masked = CAUSAL ? (kv > myq) : (kv >= S);
+            if (masked) s[kb][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = wave_xor32_max(mx);
+      const float m_new = fmaxf(m, mx * c);
+      const float ref = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m - ref);
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -ref));
+          s[kb][i] = p;
+          ls += p;
+        }
+      l = l * alpha + ls;
+      m = m_new;
+#pragma unroll
+      for (int d = 0; d < HD / 32; ++d) oacc[d] *= alpha;
+      // O^T (HD x 32) += V_tile^T P^T
+#pragma unroll
+      for (int kt = 0; kt < BC / 16; ++kt) {
+        const vec8<T> pf = acc_to_frag<T>(s[kt >> 1], 8 * (kt & 1));
+#pragma unroll
+        for (int d = 0; d < HD / 32; ++d) oacc[d] = mma<T>(VTile::frag(Vt, 32 * d + r, kt, h), pf, oacc[d]);
+      }
+    }
+    if (more) {
+      T* nb = lds + ((jt + 1) & 1) * kBuf;
+      kst.store_rows(nb, tid);
+      vst.store_transposed(nb + KTile::kElems, tid);
+    }
+    __syncthreads();
+  }
+
+  l = wave_xor32_sum(l);
+  if (myq < S) {
+    const float inv = 1.f / l;
+    T* Or = O + (size_t)bh * S * HD + (size_t)myq * HD;
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<T>(Or + 32 * d + 8 * g + 4 * h, oacc[d][4 * g] * inv, oacc[d][4 * g + 1] * inv,
+                  oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv);
+    if (LSE != nullptr && h == 0) LSE[(size_t)bh * S + myq] = (m + log2f(l)) * kLn2;
+  }
+}
+
+template <typename T, int HD, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  constexpr int NW = 4, BC = 64, BR = 32 * NW;
+  const int nqt = (a.S + BR - 1) / BR;
+  dim3 grid(nqt, a.B * a.Hq), block(NW * 64);
+  mark(a.ev, a.nev, 0, st);
+  hipLaunchKernelGGL((fwd_kernel<T, HD, BC, NW, CAUSAL>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
+                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.S, a.scale * kLog2e, nqt);
+  mark(a.ev, a.nev, 1, st);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t st) {
+  if (a.D == 64) return a.causal ? launch_fwd_t<T, 64, true>(a, st) : launch_fwd_t<T, 64, false>(a, st);
+  return a.causal ? launch_fwd_t<T, 128, true>(a, st) : launch_fwd_t<T, 128, false>(a, st);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {
+  switch (a.dtype) {
+    case 0: return launch_fwd_d<float>(a, st);
+    case 1: return launch_fwd_d<_Float16>(a, st);
+    default: return launch_fwd_d<__bf16>(a, st);
+  }
+}
+
+}  // namespace fa

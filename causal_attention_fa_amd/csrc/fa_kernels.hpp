@@ -1,0 +1,50 @@
+// fa_kernels.hpp -- internal launcher interface between the C ABI (fa_api.cpp)
+// and the kernel files.  Arguments are already validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, S, D;
+  float scale;
+  int causal;
+  int dtype;  // 0 fp32, 1 fp16, 2 bf16 (fa_dtype_t)
+  hipEvent_t* ev;  // optional timing events (fa_profile_events), nev of them
+  int nev;
+};
+
+// Records ev[i] on the stream when instrumentation asked for it.
+inline void mark(hipEvent_t* ev, int nev, int i, hipStream_t st) {
+  if (ev != nullptr && i < nev) (void)hipEventRecord(ev[i], st);
+}
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* rowdot;  // workspace: D[i] = sum_d dO[i,d] * O[i,d], [B*Hq*S] fp32
+  int B, Hq, Hkv, S, D;
+  float scale;
+  int causal;
+  int dtype;
+  hipEvent_t* ev;
+  int nev;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,130 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused causal attention library, libfa.so.
+ *
+ * The library computes scaled-dot-product attention with an online (streaming)
+ * softmax over KV tiles, never forming the S x S score matrix:
+ *
+ *   forward   O = softmax(mask(scale * Q K^T)) V,  L[i] = logsumexp of row i
+ *   backward  dQ, dK, dV of sum(dO * O), recomputing the scores from Q, K, V
+ *             and L, with the row dot products D[i] = sum_d dO[i,d] * O[i,d].
+ *
+ * Definitions: "Phase T14: 融合 Flash-Attention Kernel — Design Document"
+ * (section "什么是 flash-attention": the online-softmax recurrence, L = m + log l,
+ * the flash backward formulas; decisions ② and ③: L is the only saved forward
+ * state and D removes the softmax Jacobian) and "Phase 14: Flash Attention 2 for
+ * SM120 — Design Document" (sections "FA2 算法", "GQA 支持", "Causal Mask").
+ *
+ * Layouts (all contiguous, head dimension fastest, element type = dtype):
+ *   q, o, dO, dq      [B][Hq][S][D]
+ *   k, v, dk, dv      [B][Hkv][S][D]
+ *   lse               [B][Hq][S]        float32, natural log
+ * Query head h reads KV head h / (Hq / Hkv): groups of consecutive query heads
+ * share one KV head (GQA; Hq == Hkv is plain multi-head attention).
+ *
+ * causal = 1 masks key j for query i when j > i (the single sequence length
+ * makes top-left and bottom-right alignment the same); causal = 0 masks nothing.
+ *
+ * Precision: fp32 inputs are computed in fp32 throughout.  bf16 / fp16 inputs
+ * feed the matrix cores in their own type (P and dS are rounded to it, nearest
+ * even); every accumulation, the softmax and L are fp32.  O, dq, dk, dv are
+ * written in the input dtype.
+ *
+ * Ownership and threading: every pointer is a device pointer owned by the
+ * caller; the library allocates nothing and keeps no state between calls.
+ * All work is enqueued on `stream` and the call returns without waiting.
+ * Outputs are overwritten, never accumulated into.  Calls on different
+ * streams with disjoint outputs may run concurrently.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; on
+ * any error nothing is launched and no output is touched.
+ *   FA_ERR_INVALID_ARG   null required pointer; B, Hq, Hkv, S or D < 0;
+ *                        Hkv == 0 while B*Hq*S > 0; Hq % Hkv != 0;
+ *                        scale not finite; a pointer not 16-byte aligned;
+ *                        dtype not one of fa_dtype_t.
+ *   FA_ERR_UNSUPPORTED   D not 64 or 128; scale <= 0.
+ *   FA_ERR_WORKSPACE     workspace smaller than fa_bwd_workspace_bytes().
+ *   FA_ERR_HIP           a HIP launch reported an error (hipGetLastError).
+ * A problem with B * Hq * S == 0 is a no-op that returns FA_OK once the
+ * scalar checks above pass (pointers are not inspected then).
+ * NaN or Inf in the inputs is not checked and propagates to the outputs.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_WORKSPACE = 3,
+  FA_ERR_HIP = 4
+} fa_status_t;
+
+/*
+ * Forward pass.  Writes o and (when lse is not NULL) the per-row natural-log
+ * logsumexp of the scaled, masked scores, L[i] = m_i + log(l_i)
+ * ("Phase T14", decision ②: the only forward state the backward needs).
+ *   q, k, v : inputs, layouts above, element type dtype
+ *   o       : output [B][Hq][S][D], dtype
+ *   lse     : output [B][Hq][S] float32, or NULL to skip it
+ *   scale   : multiplies Q K^T before the softmax (1/sqrt(D) for standard
+ *             attention); must be finite and > 0
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int S, int D, float scale, int causal,
+                   fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this problem (a multiple of 256;
+ * 0 for an empty problem).  It holds the fp32 row dot products D[i].
+ * Returns 0 for arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
+
+/*
+ * Backward pass ("Phase T14", section "什么是 flash-attention" and decision ③).
+ *   q, k, v, o, lse : the forward's inputs and its unchanged outputs o and lse
+ *                     (lse must not be NULL here)
+ *   dO              : gradient of the loss with respect to o, [B][Hq][S][D]
+ *   dq, dk, dv      : outputs, same layouts and dtype as q, k, v; dk and dv of a
+ *                     KV head are summed over the query heads that read it
+ *   workspace       : device scratch of at least fa_bwd_workspace_bytes(...)
+ *                     bytes, 16-byte aligned; may be NULL when that size is 0.
+ *                     Its contents on entry are ignored and on return undefined;
+ *                     two calls in flight at once need two workspaces.
+ * The scores are recomputed as P = exp(scale * Q K^T - L); the caller must pass
+ * the same scale and causal flag as to the forward.
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int S, int D, float scale, int causal,
+                   fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a status code ("FA_OK", ...); never NULL. */
+const char* fa_status_string(fa_status_t s);
+
+/*
+ * Instrumentation for benchmarks (not part of the computation).  After
+ * fa_profile_events(ev, n) with ev != NULL, each later fa_fwd / fa_bwd call made
+ * from the same host thread records ev[0..] on its stream around every kernel
+ * it launches: fa_fwd records ev[0] before and ev[1] after its one kernel;
+ * fa_bwd records ev[0] before the row-dot kernel, ev[1] before the dK/dV
+ * kernel, ev[2] before the dQ kernel and ev[3] after it.  Indices >= n are not
+ * recorded.  The caller owns the events (created with hipEventCreate) and must
+ * keep them alive while in use; fa_profile_events(NULL, 0) turns recording off.
+ */
+void fa_profile_events(hipEvent_t* events, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */
