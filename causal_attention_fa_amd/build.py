@@ -20,9 +20,13 @@ LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
+# -amdgpu-mfma-vgpr-form=1: keep MFMA accumulators in architectural VGPRs;
+#   the default heuristic parks the long-lived dK/dV accumulators in AGPRs and
+#   then copies them to VGPRs and back around every tile's MFMAs.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

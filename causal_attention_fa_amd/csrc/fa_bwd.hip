@@ -25,12 +25,13 @@
 // Layout choices (MI355X-specific):
 //   dkdv: S = Q K^T and dP = dO V^T are formed with the wave's keys as MFMA
 //   columns, so P and dS come out of the accumulators as the B operands of
-//   dV^T += dO^T P and dK^T += Q^T dS.  Q and dO tiles are staged in LDS both
-//   row-major (A operands of S and dP) and transposed (A operands of the
-//   gradient products).  L and D of the tile's rows are staged in LDS too.
+//   dV^T += dO^T P and dK^T += Q^T dS.  Q and dO tiles are staged row-major in
+//   LDS (A operands of S and dP); the A operands of the gradient products,
+//   dO^T and Q^T, come from gfx950's LDS transpose read of the same tiles.  L
+//   and D of the tile's rows are staged in LDS too.
 //   dq: S^T = K Q^T and dP^T = V dO^T put one query row per lane pair (like
-//   the forward), and dS^T is the B operand of dQ^T += K^T dS^T; K is staged
-//   row-major and transposed, V row-major.
+//   the forward), and dS^T is the B operand of dQ^T += K^T dS^T, whose K^T
+//   operand is a transpose read of the row-major K tile.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -67,13 +68,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     int Hq, int Hkv, int S, float c, float scale) {
   constexpr int BKV = 32 * NW;
   constexpr int NT = NW * 64;
-  using QRow = RowTile<T, BQ, HD>;
-  using QTr = TrTile<T, HD, BQ>;
-  constexpr int kOffQr = 0;
-  constexpr int kOffDr = QRow::kElems;
-  constexpr int kOffQt = 2 * QRow::kElems;
-  constexpr int kOffDt = 2 * QRow::kElems + QTr::kElems;
-  constexpr int kElems = 2 * QRow::kElems + 2 * QTr::kElems;
+  using Tile = RowTile<T, BQ, HD>;
+  constexpr int kOffQ = 0;
+  constexpr int kOffD = Tile::kElems;
+  constexpr int kElems = 2 * Tile::kElems;
   __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
   __shared__ __attribute__((aligned(16))) float lds_ld[2][2][BQ];  // [buf][L*log2e, D][row]
 
@@ -89,11 +87,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   const T* Kh = K + (size_t)bg * S * HD;
   const T* Vh = V + (size_t)bg * S * HD;
 
+  // keys past the end read key S-1: their dK, dV are never stored
   vec8<T> kf[HD / 16], vf[HD / 16];
+  {
+    const size_t off = (size_t)min(mykv, S - 1) * HD + 8 * h;
 #pragma unroll
-  for (int t = 0; t < HD / 16; ++t) {
-    kf[t] = mykv < S ? load8<T>(Kh + (size_t)mykv * HD + 16 * t + 8 * h) : zero8<T>();
-    vf[t] = mykv < S ? load8<T>(Vh + (size_t)mykv * HD + 16 * t + 8 * h) : zero8<T>();
+    for (int t = 0; t < HD / 16; ++t) {
+      kf[t] = load8<T>(Kh + off + 16 * t);
+      vf[t] = load8<T>(Vh + off + 16 * t);
+    }
   }
   f32x16 dk[HD / 32], dv[HD / 32];
 #pragma unroll
@@ -116,18 +118,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     qst.load(Q + qoff, i0, S, tid);
     dost.load(dO + qoff, i0, S, tid);
     if (tid < BQ) {
-      const size_t row = ((size_t)b * Hq + hq) * S + i0 + tid;
-      const bool ok = i0 + tid < S;
-      ld_l = ok ? LSE[row] * kLog2e : 0.f;
-      ld_d = ok ? Dd[row] : 0.f;
+      const size_t row = ((size_t)b * Hq + hq) * S + min(i0 + tid, S - 1);
+      ld_l = LSE[row] * kLog2e;
+      ld_d = Dd[row];
     }
   };
   auto commit = [&](int buf) {
     T* base = lds + buf * kElems;
-    qst.store_rows(base + kOffQr, tid);
-    dost.store_rows(base + kOffDr, tid);
-    qst.store_transposed(base + kOffQt, tid);
-    dost.store_transposed(base + kOffDt, tid);
+    qst.store_rows(base + kOffQ, tid);
+    dost.store_rows(base + kOffD, tid);
     if (tid < BQ) {
       lds_ld[buf][0][tid] = ld_l;
       lds_ld[buf][1][tid] = ld_d;
@@ -144,7 +143,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     const int i0 = (first + it % per_head) * BQ;
     const bool more = it + 1 < total;
     if (more) issue(it + 1);
-    const T* base = lds + buf * kElems;
+    const T* Qs = lds + buf * kElems + kOffQ;
+    const T* dOs = lds + buf * kElems + kOffD;
     const bool active = !CAUSAL || (i0 + BQ - 1 >= kw0);
     if (active) {
       // S, dP (BQ x 32): rows = queries of the tile, columns = this wave's keys
@@ -155,10 +155,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
         dp[qb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < HD / 16; ++t) {
-          s[qb] = mma<T>(QRow::frag(base + kOffQr, 32 * qb + r, 16 * t, h), kf[t], s[qb]);
-          dp[qb] = mma<T>(QRow::frag(base + kOffDr, 32 * qb + r, 16 * t, h), vf[t], dp[qb]);
+          s[qb] = mma<T>(Tile::frag(Qs, 32 * qb + r, 16 * t, h), kf[t], s[qb]);
+          dp[qb] = mma<T>(Tile::frag(dOs, 32 * qb + r, 16 * t, h), vf[t], dp[qb]);
         }
       }
+      // queries before the key (causal) or past the end get p = 0
       const bool edge = (CAUSAL && i0 < kw0 + 31) || (i0 + BQ > S);
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb)
@@ -187,8 +188,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
         const vec8<T> sf = acc_to_frag<T>(dp[kt >> 1], 8 * (kt & 1));
 #pragma unroll
         for (int d = 0; d < HD / 32; ++d) {
-          dv[d] = mma<T>(QTr::frag(base + kOffDt, 32 * d + r, kt, h), pf, dv[d]);
-          dk[d] = mma<T>(QTr::frag(base + kOffQt, 32 * d + r, kt, h), sf, dk[d]);
+          dv[d] = mma<T>(Tile::tr_frag(dOs, kt, 32 * d, lane), pf, dv[d]);
+          dk[d] = mma<T>(Tile::tr_frag(Qs, kt, 32 * d, lane), sf, dk[d]);
         }
       }
     }
@@ -219,12 +220,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     float c, float scale, int nqt) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
-  using KRow = RowTile<T, BC, HD>;
-  using KTr = TrTile<T, HD, BC>;
+  using Tile = RowTile<T, BC, HD>;
   constexpr int kOffK = 0;
-  constexpr int kOffV = KRow::kElems;
-  constexpr int kOffKt = 2 * KRow::kElems;
-  constexpr int kElems = 2 * KRow::kElems + KTr::kElems;
+  constexpr int kOffV = Tile::kElems;
+  constexpr int kElems = 2 * Tile::kElems;
   __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
 
   const int tid = threadIdx.x;
@@ -241,14 +240,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   const int qw0 = i0 + 32 * w;
   const int myq = qw0 + r;
 
+  // query rows past the end read row S-1: their dQ is never stored
   vec8<T> qf[HD / 16], df[HD / 16];
+  const int qrow = min(myq, S - 1);
+  {
+    const size_t off = (size_t)qrow * HD + 8 * h;
 #pragma unroll
-  for (int t = 0; t < HD / 16; ++t) {
-    qf[t] = myq < S ? load8<T>(Qh + (size_t)myq * HD + 16 * t + 8 * h) : zero8<T>();
-    df[t] = myq < S ? load8<T>(dOh + (size_t)myq * HD + 16 * t + 8 * h) : zero8<T>();
+    for (int t = 0; t < HD / 16; ++t) {
+      qf[t] = load8<T>(Qh + off + 16 * t);
+      df[t] = load8<T>(dOh + off + 16 * t);
+    }
   }
-  const float lq = myq < S ? LSE[(size_t)bh * S + myq] * kLog2e : 0.f;
-  const float dq_d = myq < S ? Dd[(size_t)bh * S + myq] : 0.f;
+  const float lq = LSE[(size_t)bh * S + qrow] * kLog2e;
+  const float dq_d = Dd[(size_t)bh * S + qrow];
   f32x16 acc[HD / 32];
 #pragma unroll
   for (int d = 0; d < HD / 32; ++d) acc[d] = f32x16{};
@@ -260,7 +264,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   kst.load(Kh, 0, S, tid);
   vst.load(Vh, 0, S, tid);
   kst.store_rows(lds + kOffK, tid);
-  kst.store_transposed(lds + kOffKt, tid);
   vst.store_rows(lds + kOffV, tid);
   __syncthreads();
 
@@ -271,7 +274,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
       kst.load(Kh, j0 + BC, S, tid);
       vst.load(Vh, j0 + BC, S, tid);
     }
-    const T* base = lds + (jt & 1) * kElems;
+    const T* Ks = lds + (jt & 1) * kElems + kOffK;
+    const T* Vs = lds + (jt & 1) * kElems + kOffV;
     const bool active = !CAUSAL || j0 <= qw0 + 31;
     if (active) {
       f32x16 s[BC / 32], dp[BC / 32];
@@ -281,11 +285,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
         dp[kb] = f32x16{};
 #pragma unroll
         for (int t = 0; t < HD / 16; ++t) {
-          s[kb] = mma<T>(KRow::frag(base + kOffK, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
-          dp[kb] = mma<T>(KRow::frag(base + kOffV, 32 * kb + r, 16 * t, h), df[t], dp[kb]);
+          s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
+          dp[kb] = mma<T>(Tile::frag(Vs, 32 * kb + r, 16 * t, h), df[t], dp[kb]);
         }
       }
       const bool edge = CAUSAL ? (j0 + BC - 1 > qw0) : (j0 + BC > S);
+      const int lim = CAUSAL ? myq : S - 1;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
@@ -293,8 +298,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
           float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -lq));
           if (edge) {
             const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            const bool masked = CAUSAL ? (kv > myq) : (kv >= S);
-            p = masked ? 0.f : p;
+            p = kv > lim ? 0.f : p;
           }
           dp[kb][i] = p * (dp[kb][i] - dq_d);
         }
@@ -303,13 +307,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
       for (int kt = 0; kt < BC / 16; ++kt) {
         const vec8<T> sf = acc_to_frag<T>(dp[kt >> 1], 8 * (kt & 1));
 #pragma unroll
-        for (int d = 0; d < HD / 32; ++d) acc[d] = mma<T>(KTr::frag(base + kOffKt, 32 * d + r, kt, h), sf, acc[d]);
+        for (int d = 0; d < HD / 32; ++d) acc[d] = mma<T>(Tile::tr_frag(Ks, kt, 32 * d, lane), sf, acc[d]);
       }
     }
     if (more) {
       T* nb = lds + ((jt + 1) & 1) * kElems;
       kst.store_rows(nb + kOffK, tid);
-      kst.store_transposed(nb + kOffKt, tid);
       vst.store_rows(nb + kOffV, tid);
     }
     __syncthreads();
@@ -352,8 +355,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   {
-    // fp32 at D=128 would need 200 KiB of LDS with 64-key tiles: use 32.
-    constexpr int NW = 4, BC = (sizeof(T) == 4 && HD == 128) ? 32 : 64;
+    constexpr int NW = 4, BC = 64;
     const int nqt = (a.S + 32 * NW - 1) / (32 * NW);
     dim3 grid(nqt, a.B * a.Hq);
     mark(a.ev, a.nev, 2, st);

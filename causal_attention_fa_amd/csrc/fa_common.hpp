@@ -129,62 +129,82 @@ __device__ inline float wave_xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 
 __device__ inline float wave_xor32_sum(float x) { return x + __shfl_xor(x, 32); }
 
 // ------------------------------------------------------------------ LDS tiles
-// Row tile: ROWS x HD elements, row stride HD + 16 bytes of padding so that the
-// 32 rows read by one A-fragment load fall in different banks.
+// Row tile: ROWS x HD elements, row-major, row stride HD + 16 bytes of padding
+// so that the rows read by one row-fragment load fall in different banks.
 template <typename T, int ROWS, int HD>
 struct RowTile {
   static constexpr int kStride = HD + 16 / (int)sizeof(T);
   static constexpr int kElems = ROWS * kStride;
-  // A fragment: rows `row`, contraction (column) indices c0 + 8h + j.
+  // A or B fragment with the tile's rows as the fragment rows / columns and the
+  // tile's columns as contraction index: row `row`, columns c0 + 8h + j.
   __device__ static inline vec8<T> frag(const T* base, int row, int c0, int h) {
     return load8<T>(base + row * kStride + c0 + 8 * h);
   }
   __device__ static inline void put_unit(T* base, int row, int col, Unit<T> u) {
     *reinterpret_cast<u32x4*>(base + row * kStride + col) = u.bits;
   }
+  // Transposed fragment: the tile's rows are the contraction index and its
+  // columns the fragment rows.  Lane l = 32h + r receives, for contraction step
+  // kt, X[16kt + 8(j/4) + 4h + (j%4)][col0 + r] in slot j -- the indices that
+  // accumulator registers 8(kt%2)..8(kt%2)+7 of a 32x32 tile hold for lane
+  // half h, so it pairs with acc_to_frag().
+  __device__ static inline vec8<T> tr_frag(const T* base, int kt, int col0, int lane);
 };
 
-// Transposed tile: holds X^T for an X of COLS rows and HD columns, i.e. HD rows
-// of COLS elements (+4 elements of padding).  An A fragment of X^T for
-// contraction step kt reads, at row d, the runs [16kt + 4h, +4) and
-// [16kt + 8 + 4h, +4): exactly the indices that accumulator registers
-// 8*(kt%2) .. 8*(kt%2)+7 of a 32x32 tile hold for lane half h.
-template <typename T, int HD, int COLS>
-struct TrTile {
-  static constexpr int kStride = COLS + 4;
-  static constexpr int kElems = HD * kStride;
-  __device__ static inline vec8<T> frag(const T* base, int d, int kt, int h) {
-    const T* p = base + d * kStride + 16 * kt + 4 * h;
-    return load4x2<T>(p, p + 8);
+// 16-bit elements: gfx950's LDS transpose read.  Within each group of 16
+// lanes, lane j supplies the address of X[R0 + j/4][C0 + 4(j%4)] (4 elements)
+// and lane i receives X[R0 + k][C0 + i], k = 0..3.  Two reads (rows R0 and
+// R0 + 8) make one 8-slot fragment.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ inline vec4<T> lds_tr4(const T* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(vec4<T>, v);
+}
+
+template <typename T, int ROWS, int HD>
+__device__ inline vec8<T> RowTile<T, ROWS, HD>::tr_frag(const T* base, int kt, int col0, int lane) {
+  if constexpr (sizeof(T) == 2) {
+    const int row = 16 * kt + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const T* p = base + row * kStride + col;
+    vec4<T> a = lds_tr4<T>(p);
+    vec4<T> b = lds_tr4<T>(p + 8 * kStride);
+    return vec8<T>{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    // fp32: eight scalar reads (only the small fp32 workloads take this path)
+    const int h = lane >> 5, r = lane & 31;
+    const T* p = base + (16 * kt + 4 * h) * kStride + col0 + r;
+    vec8<T> f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] = p[(8 * (j >> 2) + (j & 3)) * kStride];
+    return f;
   }
-};
+}
 
 // ------------------------------------------------------------------ global -> LDS staging
-// A tile of ROWS rows x HD columns of a row-major [S][HD] matrix, rows at or
-// beyond `nvalid` read as zero.  Work unit: 4 rows x kEpv columns (four 16-byte
-// loads per unit).  The same registers can be written to a RowTile, a TrTile,
-// or both.
+// A tile of ROWS rows x HD columns of a row-major [S][HD] matrix.  Rows at or
+// beyond `nvalid` are loaded from row nvalid - 1 instead (every kernel masks
+// those rows' scores or never stores their results), so loads need no
+// branches.  Each thread moves whole 16-byte units through registers: load()
+// issues the global loads, store_rows() writes them to a RowTile.
 template <typename T, int ROWS, int HD, int NT>
 struct Stager {
   static constexpr int kEpv = Elem<T>::kEpv;
-  static constexpr int kUnitsPerRowGroup = HD / kEpv;
-  static constexpr int kUnits = (ROWS / 4) * kUnitsPerRowGroup;
+  static constexpr int kUnitsPerRow = HD / kEpv;
+  static constexpr int kUnits = ROWS * kUnitsPerRow;
   static constexpr int kPerThread = (kUnits + NT - 1) / NT;
-  static_assert(ROWS % 4 == 0, "rows in groups of 4");
-  Unit<T> u[kPerThread][4];
+  Unit<T> u[kPerThread];
 
   __device__ inline void load(const T* __restrict__ g, int row0, int nvalid, int tid) {
 #pragma unroll
     for (int p = 0; p < kPerThread; ++p) {
       const int unit = tid + p * NT;
       if (kUnits % NT == 0 || unit < kUnits) {
-        const int rg = unit / kUnitsPerRowGroup;
-        const int col = (unit % kUnitsPerRowGroup) * kEpv;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = row0 + 4 * rg + rr;
-          u[p][rr] = row < nvalid ? load_unit<T>(g + (size_t)row * HD + col) : zero_unit<T>();
-        }
+        const int row = min(row0 + unit / kUnitsPerRow, nvalid - 1);
+        const int col = (unit % kUnitsPerRow) * kEpv;
+        u[p] = load_unit<T>(g + (size_t)row * HD + col);
       }
     }
   }
@@ -193,46 +213,8 @@ struct Stager {
 #pragma unroll
     for (int p = 0; p < kPerThread; ++p) {
       const int unit = tid + p * NT;
-      if (kUnits % NT == 0 || unit < kUnits) {
-        const int rg = unit / kUnitsPerRowGroup;
-        const int col = (unit % kUnitsPerRowGroup) * kEpv;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) RowTile<T, ROWS, HD>::put_unit(lds, 4 * rg + rr, col, u[p][rr]);
-      }
-    }
-  }
-
-  // Transposed store: column c of the unit becomes LDS row (col + c), and the
-  // unit's 4 rows become 4 consecutive elements of that row.
-  __device__ inline void store_transposed(T* lds, int tid) const {
-    constexpr int kStride = TrTile<T, HD, ROWS>::kStride;
-#pragma unroll
-    for (int p = 0; p < kPerThread; ++p) {
-      const int unit = tid + p * NT;
-      if (kUnits % NT == 0 || unit < kUnits) {
-        const int rg = unit / kUnitsPerRowGroup;
-        const int col = (unit % kUnitsPerRowGroup) * kEpv;
-        if constexpr (sizeof(T) == 2) {
-          // 16-bit elements: element c of row rr is half (c & 1) of word c/2.
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const int w = c >> 1;
-            const int sh = (c & 1) * 16;
-            const uint32_t e0 = (u[p][0].bits[w] >> sh) & 0xFFFFu;
-            const uint32_t e1 = (u[p][1].bits[w] >> sh) & 0xFFFFu;
-            const uint32_t e2 = (u[p][2].bits[w] >> sh) & 0xFFFFu;
-            const uint32_t e3 = (u[p][3].bits[w] >> sh) & 0xFFFFu;
-            u32x2 packed{e0 | (e1 << 16), e2 | (e3 << 16)};
-            *reinterpret_cast<u32x2*>(lds + (col + c) * kStride + 4 * rg) = packed;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            u32x4 packed{u[p][0].bits[c], u[p][1].bits[c], u[p][2].bits[c], u[p][3].bits[c]};
-            *reinterpret_cast<u32x4*>(lds + (col + c) * kStride + 4 * rg) = packed;
-          }
-        }
-      }
+      if (kUnits % NT == 0 || unit < kUnits)
+        RowTile<T, ROWS, HD>::put_unit(lds, unit / kUnitsPerRow, (unit % kUnitsPerRow) * kEpv, u[p]);
     }
   }
 };

@@ -17,10 +17,14 @@
 //     probabilities P^T come out of the accumulators already laid out as the B
 //     operand of O^T += V^T P^T (no LDS round trip for P);
 //   * Q stays in registers (B operand of S^T) for the whole kernel;
-//   * K (row-major) and V (transposed) tiles are staged in LDS, double
-//     buffered: the next tile's global loads are issued before the current
-//     tile's math and written to the other buffer after it;
-//   * softmax in base 2: p = exp2(s * scale*log2e - m), m tracked in that unit;
+//   * K and V tiles are staged row-major in LDS, double buffered: the next
+//     tile's global loads are issued before the current tile's math and written
+//     to the other buffer after it; V^T fragments come from gfx950's LDS
+//     transpose read;
+//   * softmax in base 2: p = exp2(s * scale*log2e - m), m tracked in that unit,
+//     and the accumulator is rescaled only when a row's max grows by > 2^4;
+//   * the row sum l is one more MFMA per step (all-ones A operand), so it sums
+//     exactly the rounded P that multiplies V;
 //   * causal: workgroups are launched heaviest (last query tiles) first, a wave
 //     skips KV tiles that lie wholly after its rows, and the element mask is
 //     applied on diagonal tiles only.
@@ -29,15 +33,22 @@
 
 namespace fa {
 
+// Lazy rescale threshold (log2 units): the running reference m only moves
+// when some row's maximum grows by more than this, so p <= 2^kRescaleLog2.
+// The row sum l is taken from the same dtype-rounded P that multiplies V, so
+// O = sum(P~ V) / sum(P~) stays a consistent weighted average: with that, a
+// threshold of 2^4 keeps the bf16 error of eager rescaling (measured on the
+// long-context workload), while 2^8 with an unrounded l does not.
+constexpr float kRescaleLog2 = 4.f;
+
 template <typename T, int HD, int BC, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, int Hq, int Hkv, int S, float c, int nqt) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
-  using KTile = RowTile<T, BC, HD>;
-  using VTile = TrTile<T, HD, BC>;
-  constexpr int kBuf = KTile::kElems + VTile::kElems;
+  using Tile = RowTile<T, BC, HD>;
+  constexpr int kBuf = 2 * Tile::kElems;  // K tile, then V tile
   __shared__ __attribute__((aligned(16))) T lds[2 * kBuf];
 
   const int tid = threadIdx.x;
@@ -53,15 +64,23 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   const int qw0 = i0 + 32 * w;
   const int myq = qw0 + r;
 
+  // rows past the end read row S-1: their results are never stored
   vec8<T> qf[HD / 16];
+  const T* qrow = Qh + (size_t)min(myq, S - 1) * HD + 8 * h;
 #pragma unroll
-  for (int t = 0; t < HD / 16; ++t)
-    qf[t] = myq < S ? load8<T>(Qh + (size_t)myq * HD + 16 * t + 8 * h) : zero8<T>();
+  for (int t = 0; t < HD / 16; ++t) qf[t] = load8<T>(qrow + 16 * t);
 
   f32x16 oacc[HD / 32];
 #pragma unroll
   for (int d = 0; d < HD / 32; ++d) oacc[d] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  // Row sums on the matrix cores: an all-ones A operand turns O^T += V^T P^T
+  // into lacc += 1 P^T, whose every register holds sum_kv P~[kv][q] for the
+  // lane's query q (the full sum, both lane halves included).
+  f32x16 lacc = f32x16{};
+  vec8<T> ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = to_elem<T>(1.f);
+  float m = -INFINITY;
 
   const int kv_end = CAUSAL ? min(S, i0 + BR) : S;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -70,7 +89,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   kst.load(Kh, 0, S, tid);
   vst.load(Vh, 0, S, tid);
   kst.store_rows(lds, tid);
-  vst.store_transposed(lds + KTile::kElems, tid);
+  vst.store_rows(lds + Tile::kElems, tid);
   __syncthreads();
 
   for (int jt = 0; jt < ntiles; ++jt) {
@@ -81,7 +100,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       vst.load(Vh, j0 + BC, S, tid);
     }
     const T* Ks = lds + (jt & 1) * kBuf;
-    const T* Vt = Ks + KTile::kElems;
+    const T* Vs = Ks + Tile::kElems;
     const bool active = !CAUSAL || j0 <= qw0 + 31;
     if (active) {
       // S^T (BC x 32) = K_tile Q_w^T
@@ -90,17 +109,18 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       for (int kb = 0; kb < BC / 32; ++kb) {
         s[kb] = f32x16{};
 #pragma unroll
-        for (int t = 0; t < HD / 16; ++t) s[kb] = mma<T>(KTile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
+        for (int t = 0; t < HD / 16; ++t) s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
       }
+      // keys after the query (causal) or past the end (last tile) get -inf
       const bool edge = CAUSAL ? (j0 + BC - 1 > qw0) : (j0 + BC > S);
       if (edge) {
+        const int lim = CAUSAL ? myq : S - 1;
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            const bool masked = CAUSAL ? (kv > myq) : (kv >= S);
-            if (masked) s[kb][i] = -INFINITY;
+            s[kb][i] = kv > lim ? -INFINITY : s[kb][i];
           }
       }
       float mx = -INFINITY;
@@ -108,40 +128,40 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = wave_xor32_max(mx);
-      const float m_new = fmaxf(m, mx * c);
-      const float ref = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - ref);
-      float ls = 0.f;
+      mx = wave_xor32_max(mx) * c;
+      // Move the reference only when a row's max outgrows it by 2^8 (any lane:
+      // the branch is wave-uniform).  O = acc / l is exact for any reference.
+      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        lacc *= alpha;
+#pragma unroll
+        for (int d = 0; d < HD / 32; ++d) oacc[d] *= alpha;
+        m = m_new;
+      }
+      const float ref = (m == -INFINITY) ? 0.f : m;  // a row with no key yet keeps p = 0
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -ref));
-          s[kb][i] = p;
-          ls += p;
-        }
-      l = l * alpha + ls;
-      m = m_new;
-#pragma unroll
-      for (int d = 0; d < HD / 32; ++d) oacc[d] *= alpha;
-      // O^T (HD x 32) += V_tile^T P^T
+        for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -ref));
+      // O^T (HD x 32) += V_tile^T P^T ; l += 1^T P^T
 #pragma unroll
       for (int kt = 0; kt < BC / 16; ++kt) {
         const vec8<T> pf = acc_to_frag<T>(s[kt >> 1], 8 * (kt & 1));
 #pragma unroll
-        for (int d = 0; d < HD / 32; ++d) oacc[d] = mma<T>(VTile::frag(Vt, 32 * d + r, kt, h), pf, oacc[d]);
+        for (int d = 0; d < HD / 32; ++d) oacc[d] = mma<T>(Tile::tr_frag(Vs, kt, 32 * d, lane), pf, oacc[d]);
+        lacc = mma<T>(ones, pf, lacc);
       }
     }
     if (more) {
       T* nb = lds + ((jt + 1) & 1) * kBuf;
       kst.store_rows(nb, tid);
-      vst.store_transposed(nb + KTile::kElems, tid);
+      vst.store_rows(nb + Tile::kElems, tid);
     }
     __syncthreads();
   }
 
-  l = wave_xor32_sum(l);
+  const float l = lacc[0];
   if (myq < S) {
     const float inv = 1.f / l;
     T* Or = O + (size_t)bh * S * HD + (size_t)myq * HD;
