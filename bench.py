@@ -241,12 +241,25 @@ def main():
     ap.add_argument("--workload", default=LONG_CONTEXT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-memory", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a reference "
+                         "dispatch for scaling HBM byte counters); not part of the timed steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
               f"multi-GPU path; the attention shards by (batch, KV head) with no communication.",
               file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy_mib > 0:
+        import torch
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     w = WORKLOADS[args.workload]
     if not w.backward:
         raise SystemExit(f"{w.name} is a forward-only workload; bench times fwd+bwd")

@@ -65,7 +65,7 @@ template <typename T, int HD, int BQ, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dK, T* __restrict__ dV,
-    int Hq, int Hkv, int S, float c, float scale) {
+    int Hq, int Hkv, int S, float c, float scale, int nkt) {
   constexpr int BKV = 32 * NW;
   constexpr int NT = NW * 64;
   using Tile = RowTile<T, BQ, HD>;
@@ -77,8 +77,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
-  const int kvt = blockIdx.x;  // small key tiles see the most queries: launched first
-  const int bg = blockIdx.y;   // b * Hkv + hkv
+  // work item: (b*Hkv + hkv) major, key tiles in order within a group (small
+  // key tiles see the most queries: launched first); one XCD takes a
+  // contiguous run, so the group's Q and dO stream through one L2
+  const int work = xcd_slice(blockIdx.x, gridDim.x);
+  const int bg = work / nkt;
+  const int kvt = work - bg * nkt;
   const int b = bg / Hkv, hkv = bg - b * Hkv;
   const int G = Hq / Hkv;
   const int kv0 = kvt * BKV;
@@ -111,9 +115,16 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
 
   Stager<T, BQ, HD, NT> qst, dost;
   float ld_l = 0.f, ld_d = 0.f;
-  auto issue = [&](int it) {
-    const int hq = hkv * G + it / per_head;
-    const int i0 = (first + it % per_head) * BQ;
+  // (query head, query tile) of an iteration, advanced without divisions
+  int cur_hq = hkv * G, cur_qt = first;      // the tile in LDS buffer `it & 1`
+  int nxt_hq = cur_hq, nxt_qt = cur_qt;      // the tile being prefetched
+  auto advance = [&](int& hq, int& qt) {
+    if (++qt == nqt) {
+      qt = first;
+      ++hq;
+    }
+  };
+  auto issue = [&](int hq, int i0) {
     const size_t qoff = ((size_t)b * Hq + hq) * S * HD;
     qst.load(Q + qoff, i0, S, tid);
     dost.load(dO + qoff, i0, S, tid);
@@ -134,15 +145,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   };
 
   if (total > 0) {
-    issue(0);
+    issue(cur_hq, cur_qt * BQ);
     commit(0);
   }
   __syncthreads();
   for (int it = 0; it < total; ++it) {
     const int buf = it & 1;
-    const int i0 = (first + it % per_head) * BQ;
+    const int i0 = cur_qt * BQ;
     const bool more = it + 1 < total;
-    if (more) issue(it + 1);
+    if (more) {
+      advance(nxt_hq, nxt_qt);
+      issue(nxt_hq, nxt_qt * BQ);
+    }
     const T* Qs = lds + buf * kElems + kOffQ;
     const T* dOs = lds + buf * kElems + kOffD;
     const bool active = !CAUSAL || (i0 + BQ - 1 >= kw0);
@@ -194,6 +208,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
       }
     }
     if (more) commit(buf ^ 1);
+    advance(cur_hq, cur_qt);
     __syncthreads();
   }
 
@@ -228,8 +243,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
-  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int bh = blockIdx.y;
+  const int work = xcd_slice(blockIdx.x, gridDim.x);  // head-major, heaviest tile first
+  const int bh = work / nqt;
+  const int qt = CAUSAL ? (nqt - 1 - (work - bh * nqt)) : (work - bh * nqt);
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hkv = hq / (Hq / Hkv);
   const T* Qh = Q + (size_t)bh * S * HD;
@@ -346,18 +362,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   {
     constexpr int NW = 4, BQ = (HD == 128 || sizeof(T) == 4) ? 32 : 64;
     const int nkt = (a.S + 32 * NW - 1) / (32 * NW);
-    dim3 grid(nkt, a.B * a.Hkv);
+    dim3 grid(nkt * a.B * a.Hkv);
     mark(a.ev, a.nev, 1, st);
     hipLaunchKernelGGL((dkdv_kernel<T, HD, BQ, NW, CAUSAL>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dk,
-                       (T*)a.dv, a.Hq, a.Hkv, a.S, c, a.scale);
+                       (T*)a.dv, a.Hq, a.Hkv, a.S, c, a.scale, nkt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     constexpr int NW = 4, BC = 64;
     const int nqt = (a.S + 32 * NW - 1) / (32 * NW);
-    dim3 grid(nqt, a.B * a.Hq);
+    dim3 grid(nqt * a.B * a.Hq);
     mark(a.ev, a.nev, 2, st);
     hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dq,

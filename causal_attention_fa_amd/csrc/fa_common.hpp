@@ -125,6 +125,18 @@ __device__ inline vec8<T> acc_to_frag(const f32x16& acc, int base) {
   return f;
 }
 
+// Workgroup order for MI355X's 8 XCDs.  The dispatcher hands consecutive
+// workgroup ids to the XCDs round-robin (id % 8), and each XCD has its own L2.
+// Returns the work item a workgroup should take so that XCD x processes the
+// contiguous slice [x*N/8, (x+1)*N/8) of a work list ordered by reuse (all
+// tiles of one head or KV group together), in list order.  A bijection on
+// [0, N); the last N % 8 ids keep their own index.
+__device__ inline int xcd_slice(int id, int n) {
+  const int per = n >> 3;
+  if (id >= (per << 3)) return id;
+  return (id & 7) * per + (id >> 3);
+}
+
 __device__ inline float wave_xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ inline float wave_xor32_sum(float x) { return x + __shfl_xor(x, 32); }
 

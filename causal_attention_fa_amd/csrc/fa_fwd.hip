@@ -27,7 +27,9 @@
 //     exactly the rounded P that multiplies V;
 //   * causal: workgroups are launched heaviest (last query tiles) first, a wave
 //     skips KV tiles that lie wholly after its rows, and the element mask is
-//     applied on diagonal tiles only.
+//     applied on diagonal tiles only;
+//   * each XCD takes a contiguous run of heads, so the query heads of a KV
+//     group stream that group's K/V through one L2.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -53,8 +55,11 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
-  const int qt = CAUSAL ? (nqt - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-  const int bh = blockIdx.y;
+  // work item: (b*Hq + hq) major, query tiles heaviest first within a head;
+  // one XCD takes a contiguous run of heads (a KV group for GQA)
+  const int work = xcd_slice(blockIdx.x, gridDim.x);
+  const int bh = work / nqt;
+  const int qt = CAUSAL ? (nqt - 1 - (work - bh * nqt)) : (work - bh * nqt);
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hkv = hq / (Hq / Hkv);
   const T* Qh = Q + (size_t)bh * S * HD;
@@ -179,7 +184,7 @@ template <typename T, int HD, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   constexpr int NW = 4, BC = 64, BR = 32 * NW;
   const int nqt = (a.S + BR - 1) / BR;
-  dim3 grid(nqt, a.B * a.Hq), block(NW * 64);
+  dim3 grid(nqt * a.B * a.Hq), block(NW * 64);
   mark(a.ev, a.nev, 0, st);
   hipLaunchKernelGGL((fwd_kernel<T, HD, BC, NW, CAUSAL>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.S, a.scale * kLog2e, nqt);
