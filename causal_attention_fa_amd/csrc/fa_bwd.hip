@@ -25,8 +25,9 @@
 // Layout choices (MI355X-specific):
 //   dkdv: S = Q K^T and dP = dO V^T are formed with the wave's keys as MFMA
 //   columns, so P and dS come out of the accumulators as the B operands of
-//   dV^T += dO^T P and dK^T += Q^T dS.  Q and dO tiles are staged row-major in
-//   LDS (A operands of S and dP); the A operands of the gradient products,
+//   dV^T += dO^T P and dK^T += Q^T dS.  Q and dO tiles are staged row-major
+//   (XOR-swizzled, direct global->LDS loads) in LDS (A operands of S and dP);
+//   the A operands of the gradient products,
 //   dO^T and Q^T, come from gfx950's LDS transpose read of the same tiles.  L
 //   and D of the tile's rows are staged in LDS too.
 //   dq: S^T = K Q^T and dP^T = V dO^T put one query row per lane pair (like
@@ -113,7 +114,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   const int per_head = nqt - first;
   const int total = G * per_head;
 
-  Stager<T, BQ, HD, NT> qst, dost;
+  TileLoader<T, BQ, HD, NT> qld, dold;
+  qld.init(tid);
+  dold.init(tid);
   float ld_l = 0.f, ld_d = 0.f;
   // (query head, query tile) of an iteration, advanced without divisions
   int cur_hq = hkv * G, cur_qt = first;      // the tile in LDS buffer `it & 1`
@@ -124,10 +127,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
       ++hq;
     }
   };
-  auto issue = [&](int hq, int i0) {
+  auto issue = [&](int hq, int i0, int buf) {
     const size_t qoff = ((size_t)b * Hq + hq) * S * HD;
-    qst.load(Q + qoff, i0, S, tid);
-    dost.load(dO + qoff, i0, S, tid);
+    T* base = lds + buf * kElems;
+    qld.issue(Q + qoff, i0, S, base + kOffQ, tid);
+    dold.issue(dO + qoff, i0, S, base + kOffD, tid);
     if (tid < BQ) {
       const size_t row = ((size_t)b * Hq + hq) * S + min(i0 + tid, S - 1);
       ld_l = LSE[row] * kLog2e;
@@ -135,9 +139,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     }
   };
   auto commit = [&](int buf) {
-    T* base = lds + buf * kElems;
-    qst.store_rows(base + kOffQ, tid);
-    dost.store_rows(base + kOffD, tid);
+    qld.land(tid);
+    dold.land(tid);
     if (tid < BQ) {
       lds_ld[buf][0][tid] = ld_l;
       lds_ld[buf][1][tid] = ld_d;
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   };
 
   if (total > 0) {
-    issue(cur_hq, cur_qt * BQ);
+    issue(cur_hq, cur_qt * BQ, 0);
     commit(0);
   }
   __syncthreads();
@@ -153,9 +156,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     const int buf = it & 1;
     const int i0 = cur_qt * BQ;
     const bool more = it + 1 < total;
-    if (more) {
+    if (more) {  // the other buffer was last read before the previous barrier
       advance(nxt_hq, nxt_qt);
-      issue(nxt_hq, nxt_qt * BQ);
+      issue(nxt_hq, nxt_qt * BQ, buf ^ 1);
     }
     const T* Qs = lds + buf * kElems + kOffQ;
     const T* dOs = lds + buf * kElems + kOffD;
@@ -276,60 +279,62 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   const int kv_end = CAUSAL ? min(S, i0 + BR) : S;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  Stager<T, BC, HD, NT> kst, vst;
-  kst.load(Kh, 0, S, tid);
-  vst.load(Vh, 0, S, tid);
-  kst.store_rows(lds + kOffK, tid);
-  vst.store_rows(lds + kOffV, tid);
+  TileLoader<T, BC, HD, NT> kld, vld;
+  kld.init(tid);
+  vld.init(tid);
+  kld.issue(Kh, 0, S, lds + kOffK, tid);
+  vld.issue(Vh, 0, S, lds + kOffV, tid);
+  kld.land(tid);
+  vld.land(tid);
   __syncthreads();
 
   for (int jt = 0; jt < ntiles; ++jt) {
     const int j0 = jt * BC;
     const bool more = jt + 1 < ntiles;
-    if (more) {
-      kst.load(Kh, j0 + BC, S, tid);
-      vst.load(Vh, j0 + BC, S, tid);
+    if (more) {  // the other buffer was last read before the previous barrier
+      T* nb = lds + ((jt + 1) & 1) * kElems;
+      kld.issue(Kh, j0 + BC, S, nb + kOffK, tid);
+      vld.issue(Vh, j0 + BC, S, nb + kOffV, tid);
     }
     const T* Ks = lds + (jt & 1) * kElems + kOffK;
     const T* Vs = lds + (jt & 1) * kElems + kOffV;
     const bool active = !CAUSAL || j0 <= qw0 + 31;
     if (active) {
-      f32x16 s[BC / 32], dp[BC / 32];
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < HD / 16; ++t) {
-          s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
-          dp[kb] = mma<T>(Tile::frag(Vs, 32 * kb + r, 16 * t, h), df[t], dp[kb]);
-        }
-      }
       const bool edge = CAUSAL ? (j0 + BC - 1 > qw0) : (j0 + BC > S);
       const int lim = CAUSAL ? myq : S - 1;
+      // one 32-key block at a time: its S^T, dP^T and dS^T are dead before the
+      // next block's are formed, which halves the accumulator registers
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+      for (int kb = 0; kb < BC / 32; ++kb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t) {
+          s = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s);
+          dp = mma<T>(Tile::frag(Vs, 32 * kb + r, 16 * t, h), df[t], dp);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -lq));
+          float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lq));
           if (edge) {
             const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
             p = kv > lim ? 0.f : p;
           }
-          dp[kb][i] = p * (dp[kb][i] - dq_d);
+          dp[i] = p * (dp[i] - dq_d);
         }
-      // dQ^T (HD x 32) += K_tile^T dS^T
+        // dQ^T (HD x 32) += K_block^T dS^T
 #pragma unroll
-      for (int kt = 0; kt < BC / 16; ++kt) {
-        const vec8<T> sf = acc_to_frag<T>(dp[kt >> 1], 8 * (kt & 1));
+        for (int kk = 0; kk < 2; ++kk) {
+          const vec8<T> sf = acc_to_frag<T>(dp, 8 * kk);
 #pragma unroll
-        for (int d = 0; d < HD / 32; ++d) acc[d] = mma<T>(Tile::tr_frag(Ks, kt, 32 * d, lane), sf, acc[d]);
+          for (int d = 0; d < HD / 32; ++d)
+            acc[d] = mma<T>(Tile::tr_frag(Ks, 2 * kb + kk, 32 * d, lane), sf, acc[d]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (more) {
-      T* nb = lds + ((jt + 1) & 1) * kElems;
-      kst.store_rows(nb + kOffK, tid);
-      vst.store_rows(nb + kOffV, tid);
+      kld.land(tid);
+      vld.land(tid);
     }
     __syncthreads();
   }

@@ -141,19 +141,49 @@ __device__ inline float wave_xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 
 __device__ inline float wave_xor32_sum(float x) { return x + __shfl_xor(x, 32); }
 
 // ------------------------------------------------------------------ LDS tiles
-// Row tile: ROWS x HD elements, row-major, row stride HD + 16 bytes of padding
-// so that the rows read by one row-fragment load fall in different banks.
+// Row tile: ROWS x HD elements, row-major.
+//
+// 16-bit elements: rows are packed (stride HD) and the 16-byte chunks of each
+// row are XOR-swizzled, physical chunk = chunk ^ swz(row).  With 64 banks of
+// 4 bytes, 16-byte accesses served 16 lanes at a time and 8-byte (and
+// transpose) accesses 32 lanes at a time, this makes every access pattern the
+// kernels use conflict-free: a row fragment (16 consecutive rows, one chunk),
+// a transpose read (4 consecutive rows, an aligned quad of chunks) and a
+// staging store (whole rows).  A plain 16-byte row padding leaves the
+// transpose reads 4-way conflicted.
+//   256-byte rows (16 chunks): swz = 4 (row & 3) + ((row >> 2) & 3)
+//   128-byte rows ( 8 chunks): swz = 4 ((row >> 1) & 1) + ((row >> 2) & 3)
+// fp32 elements: rows padded by 16 bytes, no swizzle.
 template <typename T, int ROWS, int HD>
 struct RowTile {
-  static constexpr int kStride = HD + 16 / (int)sizeof(T);
+  static constexpr bool kSwizzle = sizeof(T) == 2;
+  static constexpr int kChunks = HD * (int)sizeof(T) / 16;
+  static constexpr int kEpc = 16 / (int)sizeof(T);  // elements per chunk
+  static constexpr int kStride = kSwizzle ? HD : HD + kEpc;
   static constexpr int kElems = ROWS * kStride;
+  static_assert(!kSwizzle || kChunks == 16 || kChunks == 8, "swizzle defined for 128/256-byte rows");
+
+  __device__ static inline int swz(int row) {
+    if constexpr (kChunks == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+  // element offset of (row, col); col's chunk is swizzled, its offset within
+  // the chunk is kept
+  __device__ static inline int at(int row, int col) {
+    if constexpr (kSwizzle) {
+      const int ch = col / kEpc;
+      return row * kStride + ((ch ^ swz(row)) * kEpc) + (col % kEpc);
+    } else {
+      return row * kStride + col;
+    }
+  }
   // A or B fragment with the tile's rows as the fragment rows / columns and the
   // tile's columns as contraction index: row `row`, columns c0 + 8h + j.
   __device__ static inline vec8<T> frag(const T* base, int row, int c0, int h) {
-    return load8<T>(base + row * kStride + c0 + 8 * h);
+    return load8<T>(base + at(row, c0 + 8 * h));
   }
   __device__ static inline void put_unit(T* base, int row, int col, Unit<T> u) {
-    *reinterpret_cast<u32x4*>(base + row * kStride + col) = u.bits;
+    *reinterpret_cast<u32x4*>(base + at(row, col)) = u.bits;
   }
   // Transposed fragment: the tile's rows are the contraction index and its
   // columns the fragment rows.  Lane l = 32h + r receives, for contraction step
@@ -180,17 +210,15 @@ __device__ inline vec8<T> RowTile<T, ROWS, HD>::tr_frag(const T* base, int kt, i
   if constexpr (sizeof(T) == 2) {
     const int row = 16 * kt + 4 * (lane >> 5) + ((lane & 15) >> 2);
     const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const T* p = base + row * kStride + col;
-    vec4<T> a = lds_tr4<T>(p);
-    vec4<T> b = lds_tr4<T>(p + 8 * kStride);
+    vec4<T> a = lds_tr4<T>(base + at(row, col));
+    vec4<T> b = lds_tr4<T>(base + at(row + 8, col));
     return vec8<T>{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   } else {
     // fp32: eight scalar reads (only the small fp32 workloads take this path)
     const int h = lane >> 5, r = lane & 31;
-    const T* p = base + (16 * kt + 4 * h) * kStride + col0 + r;
     vec8<T> f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = p[(8 * (j >> 2) + (j & 3)) * kStride];
+    for (int j = 0; j < 8; ++j) f[j] = base[at(16 * kt + 4 * h + 8 * (j >> 2) + (j & 3), col0 + r)];
     return f;
   }
 }
@@ -229,6 +257,75 @@ struct Stager {
         RowTile<T, ROWS, HD>::put_unit(lds, unit / kUnitsPerRow, (unit % kUnitsPerRow) * kEpv, u[p]);
     }
   }
+};
+
+// ------------------------------------------------------------------ tile loader
+// Moves a ROWS x HD tile of a row-major [S][HD] matrix into a RowTile.  Rows
+// at or beyond `nvalid` read row nvalid - 1 (every kernel masks or discards
+// them).  Interface: issue() starts the transfer into an LDS tile, land()
+// completes it; the tile may be read after land() and a workgroup barrier.
+//
+// 16-bit elements use gfx950's direct global -> LDS loads (16 bytes per lane,
+// no VGPR staging): instruction p of wave w writes LDS bytes
+// [(p*NW + w)*1024, +1024) of the tile, lane l the 16 bytes at +16 l, so each
+// lane loads the logical chunk that the swizzle places at its physical slot
+// (a permutation within one row: the loads stay coalesced).  The data is in
+// LDS once the wave's vector-memory counter drains, which the barrier's
+// release fence waits for; land() has nothing to do.
+// fp32 elements go through registers (Stager) into the padded tile.
+template <typename T, int ROWS, int HD, int NT, bool DIRECT = (sizeof(T) == 2)>
+struct TileLoader {
+  Stager<T, ROWS, HD, NT> st;
+  T* dst = nullptr;
+  __device__ inline void init(int) {}
+  __device__ inline void issue(const T* __restrict__ g, int row0, int nvalid, T* lds, int tid) {
+    st.load(g, row0, nvalid, tid);
+    dst = lds;
+  }
+  __device__ inline void land(int tid) { st.store_rows(dst, tid); }
+};
+
+template <typename T, int ROWS, int HD, int NT>
+struct TileLoader<T, ROWS, HD, NT, true> {
+  using Tile = RowTile<T, ROWS, HD>;
+  static constexpr int kNW = NT / 64;
+  static constexpr int kRowBytes = HD * 2;
+  static constexpr int kInstr = ROWS * kRowBytes / (kNW * 1024);
+  static_assert(ROWS * kRowBytes % (kNW * 1024) == 0, "tile must be whole 1 KiB wave slices");
+  int off[kInstr];  // element offset (row * HD + logical column) this lane loads, per instruction
+  int wslot;        // wave index (uniform)
+
+  __device__ inline void init(int tid) {
+    wslot = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+#pragma unroll
+    for (int p = 0; p < kInstr; ++p) {
+      const int byte = (p * kNW + wslot) * 1024 + 16 * lane;
+      const int row = byte / kRowBytes;
+      const int pch = (byte % kRowBytes) / 16;
+      off[p] = row * HD + (pch ^ Tile::swz(row)) * 8;
+    }
+  }
+  __device__ inline void issue(const T* __restrict__ g, int row0, int nvalid, T* lds, int) {
+    if (row0 + ROWS <= nvalid) {
+      const T* gb = g + (size_t)row0 * HD;
+#pragma unroll
+      for (int p = 0; p < kInstr; ++p)
+        __builtin_amdgcn_global_load_lds((const void*)(gb + off[p]),
+                                         (__attribute__((address_space(3))) void*)(lds + (p * kNW + wslot) * 512),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int p = 0; p < kInstr; ++p) {
+        const int r = off[p] / HD;
+        const int row = min(row0 + r, nvalid - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)row * HD + (off[p] - r * HD)),
+                                         (__attribute__((address_space(3))) void*)(lds + (p * kNW + wslot) * 512),
+                                         16, 0, 0);
+      }
+    }
+  }
+  __device__ inline void land(int) {}
 };
 
 // Stores 4 consecutive output elements (fp32 values) at p.

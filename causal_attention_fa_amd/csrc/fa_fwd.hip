@@ -17,10 +17,9 @@
 //     probabilities P^T come out of the accumulators already laid out as the B
 //     operand of O^T += V^T P^T (no LDS round trip for P);
 //   * Q stays in registers (B operand of S^T) for the whole kernel;
-//   * K and V tiles are staged row-major in LDS, double buffered: the next
-//     tile's global loads are issued before the current tile's math and written
-//     to the other buffer after it; V^T fragments come from gfx950's LDS
-//     transpose read;
+//   * K and V tiles are staged row-major (XOR-swizzled) in LDS, double
+//     buffered: the next tile's direct global->LDS loads are issued before the
+//     current tile's math; V^T fragments come from gfx950's LDS transpose read;
 //   * softmax in base 2: p = exp2(s * scale*log2e - m), m tracked in that unit,
 //     and the accumulator is rescaled only when a row's max grows by > 2^4;
 //   * the row sum l is one more MFMA per step (all-ones A operand), so it sums
@@ -90,19 +89,22 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   const int kv_end = CAUSAL ? min(S, i0 + BR) : S;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  Stager<T, BC, HD, NT> kst, vst;
-  kst.load(Kh, 0, S, tid);
-  vst.load(Vh, 0, S, tid);
-  kst.store_rows(lds, tid);
-  vst.store_rows(lds + Tile::kElems, tid);
+  TileLoader<T, BC, HD, NT> kld, vld;
+  kld.init(tid);
+  vld.init(tid);
+  kld.issue(Kh, 0, S, lds, tid);
+  vld.issue(Vh, 0, S, lds + Tile::kElems, tid);
+  kld.land(tid);
+  vld.land(tid);
   __syncthreads();
 
   for (int jt = 0; jt < ntiles; ++jt) {
     const int j0 = jt * BC;
     const bool more = jt + 1 < ntiles;
-    if (more) {
-      kst.load(Kh, j0 + BC, S, tid);
-      vst.load(Vh, j0 + BC, S, tid);
+    if (more) {  // the other buffer was last read before the previous barrier
+      T* nb = lds + ((jt + 1) & 1) * kBuf;
+      kld.issue(Kh, j0 + BC, S, nb, tid);
+      vld.issue(Vh, j0 + BC, S, nb + Tile::kElems, tid);
     }
     const T* Ks = lds + (jt & 1) * kBuf;
     const T* Vs = Ks + Tile::kElems;
@@ -159,9 +161,8 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       }
     }
     if (more) {
-      T* nb = lds + ((jt + 1) & 1) * kBuf;
-      kst.store_rows(nb, tid);
-      vst.store_rows(nb + Tile::kElems, tid);
+      kld.land(tid);
+      vld.land(tid);
     }
     __syncthreads();
   }
