@@ -73,7 +73,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   constexpr int kOffQ = 0;
   constexpr int kOffD = Tile::kElems;
   constexpr int kElems = 2 * Tile::kElems;
+  using VTile = RowTile<T, BKV, HD>;
   __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
+  __shared__ __attribute__((aligned(16))) T lds_v[VTile::kElems];  // this workgroup's V rows
   __shared__ __attribute__((aligned(16))) float lds_ld[2][2][BQ];  // [buf][L*log2e, D][row]
 
   const int tid = threadIdx.x;
@@ -92,15 +94,20 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   const T* Kh = K + (size_t)bg * S * HD;
   const T* Vh = V + (size_t)bg * S * HD;
 
-  // keys past the end read key S-1: their dK, dV are never stored
-  vec8<T> kf[HD / 16], vf[HD / 16];
+  // keys past the end read key S-1: their dK, dV are never stored.  K stays
+  // in registers (B operand of S); V, the B operand of dP, is read from LDS
+  // each tile, which keeps the kernel within 256 VGPRs (two workgroups per CU)
+  vec8<T> kf[HD / 16];
   {
     const size_t off = (size_t)min(mykv, S - 1) * HD + 8 * h;
 #pragma unroll
-    for (int t = 0; t < HD / 16; ++t) {
-      kf[t] = load8<T>(Kh + off + 16 * t);
-      vf[t] = load8<T>(Vh + off + 16 * t);
-    }
+    for (int t = 0; t < HD / 16; ++t) kf[t] = load8<T>(Kh + off + 16 * t);
+  }
+  {
+    TileLoader<T, BKV, HD, NT> vld;
+    vld.init(tid);
+    vld.issue(Vh, kv0, S, lds_v, tid);
+    vld.land(tid);  // published by the first barrier below
   }
   f32x16 dk[HD / 32], dv[HD / 32];
 #pragma unroll
@@ -173,7 +180,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
 #pragma unroll
         for (int t = 0; t < HD / 16; ++t) {
           s[qb] = mma<T>(Tile::frag(Qs, 32 * qb + r, 16 * t, h), kf[t], s[qb]);
-          dp[qb] = mma<T>(Tile::frag(dOs, 32 * qb + r, 16 * t, h), vf[t], dp[qb]);
+          dp[qb] = mma<T>(Tile::frag(dOs, 32 * qb + r, 16 * t, h), VTile::frag(lds_v, 32 * w + r, 16 * t, h),
+                          dp[qb]);
         }
       }
       // queries before the key (causal) or past the end get p = 0
