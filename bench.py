@@ -82,6 +82,20 @@ def algorithmic_work(w):
     }
 
 
+def committed_traffic(w):
+    """Per-launch HBM bytes of each kernel from the committed counter profile of this workload,
+    if it was taken on exactly the current kernel sources (else None: the kernels changed)."""
+    from causal_attention_fa_amd.build import source_fingerprint
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    if prof.get("source_sha256") != source_fingerprint():
+        return None
+    return prof
+
+
 def run_gpu(w, steps, warmup):
     import numpy as np  # noqa: F401
     import torch
@@ -283,9 +297,22 @@ def main():
                           "frac": round(a / peak, 4)}
     dom = max(KERNELS, key=lambda n: kms[n])
     kd = kernels[dom]
+    prof = committed_traffic(w)
+    traffic = None
+    if prof is not None:
+        for n in KERNELS:
+            t = prof["kernels"].get(n)
+            if t is not None:
+                kernels[n]["hbm_bytes"] = t["fetch_bytes"] + t["write_bytes"]
+        if dom in prof["kernels"]:
+            traffic = prof["kernels"][dom]["fetch_bytes"] + prof["kernels"][dom]["write_bytes"]
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"],
                 "peak": PEAK_HBM_GBS if kd["bound"] == "hbm" else peak, "unit": kd["unit"], "frac": kd["frac"],
-                "traffic": None,
+                "traffic": traffic,
+                "traffic_note": ("HBM bytes per launch: rocprofv3 FETCH_SIZE and WRITE_SIZE, each scaled by the "
+                                 "ratio a plain copy of known size reads on the same counter; from "
+                                 f"profiles/hbm_traffic_{w.name}.json, taken on these exact kernel sources")
+                if traffic is not None else "no counter profile for the current kernel sources",
                 "work_per_launch": work[dom],
                 "work_note": "fwd 4*D, dkdv 8*D, dq 2*D flops per visited causal pair; rowdot bytes = read O, dO "
                              "+ write D"}

@@ -31,6 +31,21 @@ HIP_FLAGS = [
 ]
 
 
+def source_fingerprint() -> str:
+    """sha256 over the kernel sources, the public header and the compile flags: identifies
+    the code a measurement (e.g. an HBM-traffic counter profile) was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    h.update(" ".join(HIP_FLAGS[:-1]).encode())  # the include path differs between machines
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "fa.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):

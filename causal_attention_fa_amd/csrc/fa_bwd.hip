@@ -125,12 +125,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   qld.init(tid);
   dold.init(tid);
   float ld_l = 0.f, ld_d = 0.f;
-  // (query head, query tile) of an iteration, advanced without divisions
-  int cur_hq = hkv * G, cur_qt = first;      // the tile in LDS buffer `it & 1`
+  // (query head, query tile) of an iteration, advanced without divisions.
+  // Query tiles are walked from the last one down: every workgroup of a KV
+  // group then starts on the same tile and they move through Q / dO nearly in
+  // step, so the tiles in use at any time stay few and hit in the XCD's L2.
+  int cur_hq = hkv * G, cur_qt = nqt - 1;    // the tile in LDS buffer `it & 1`
   int nxt_hq = cur_hq, nxt_qt = cur_qt;      // the tile being prefetched
   auto advance = [&](int& hq, int& qt) {
-    if (++qt == nqt) {
-      qt = first;
+    if (--qt < first) {
+      qt = nqt - 1;
       ++hq;
     }
   };
