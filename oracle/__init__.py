@@ -26,5 +26,8 @@ from .dense import (  # noqa: F401
     sdpa_backward,
     sdpa_dq_rows,
     softmax_probs,
+    visible,
+    sdpa_forward_varlen,
+    sdpa_backward_varlen,
 )
 from .tiled import online_forward, online_backward  # noqa: F401

@@ -47,69 +47,101 @@ def _kv_head(h: int, Hq: int, Hkv: int) -> int:
     return h // (Hq // Hkv)
 
 
-def softmax_probs(q_rows, rows, k_head, scale, causal):
-    """Rows of P and L for the query rows ``rows`` (their positions 0..S-1).
+def visible(rows, cols, causal, offset=0, window=None):
+    """Boolean (len(rows), len(cols)) mask: key j visible to query i.
 
-    q_rows: (n, D) query vectors of those rows; k_head: (S, D) keys of the
+    causal: j <= i + offset, with offset = Skv - Sq (bottom-right alignment;
+    0 when queries and keys have one length).  window (>= 0): also
+    j >= i + offset - window.  Sources: the element mask of "Phase T14"
+    (section 什么是 flash-attention) and "Phase 14" (section Causal Mask, which
+    aligns a longer key sequence with kv_offset = kv_len - q_len).  The window
+    is the sliding-window mask that "FlashAttention 与 SDPA Backend" lists in
+    its support matrix; its left edge i + offset - window is a reading.
+    """
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.asarray(cols, dtype=np.int64)[None, :]
+    vis = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+    if causal:
+        vis &= j <= i + offset
+    if window is not None:
+        vis &= j >= i + offset - window
+    return vis
+
+
+def softmax_probs(q_rows, rows, k_head, scale, causal, offset=0, window=None):
+    """Rows of P and L for the query rows ``rows`` (their positions 0..Sq-1).
+
+    q_rows: (n, D) query vectors of those rows; k_head: (Skv, D) keys of the
     KV head they read.  Returns (P, L, ncols) where P is (n, ncols): columns at
     or beyond ``ncols`` are all masked (causal) and so P is zero there.
+    A row with no visible key gets P = 0 and L = -inf (its softmax is empty).
     """
     rows = np.asarray(rows, dtype=np.int64)
     q_rows = _f64(q_rows)
     k_head = _f64(k_head)
-    S = k_head.shape[0]
-    ncols = int(rows.max()) + 1 if causal else S
+    Skv = k_head.shape[0]
+    ncols = min(Skv, int(rows.max()) + offset + 1) if causal else Skv
+    ncols = max(ncols, 0)
+    n = rows.shape[0]
+    if ncols == 0:
+        return np.zeros((n, 0)), np.full(n, -np.inf), 0
     sc = scale * (q_rows @ k_head[:ncols].T)
-    if causal:
-        sc = np.where(np.arange(ncols)[None, :] > rows[:, None], -np.inf, sc)
-    m = sc.max(axis=1, keepdims=True)
+    vis = visible(rows, np.arange(ncols), causal, offset, window)
+    sc = np.where(vis, sc, -np.inf)
+    any_vis = vis.any(axis=1)
+    m = np.where(any_vis, sc.max(axis=1), 0.0)[:, None]
     e = np.exp(sc - m)
     z = e.sum(axis=1, keepdims=True)
-    return e / z, (m + np.log(z))[:, 0], ncols
+    P = np.where(any_vis[:, None], e / np.where(z > 0, z, 1.0), 0.0)
+    with np.errstate(divide="ignore"):
+        L = np.where(any_vis, (m + np.log(np.where(z > 0, z, 1.0)))[:, 0], -np.inf)
+    return P, L, ncols
 
 
 def _check_shapes(q, k, v):
-    B, Hq, S, D = q.shape
-    if k.shape[0] != B or k.shape[2:] != (S, D) or v.shape != k.shape:
-        raise ValueError("q is [B,Hq,S,D]; k and v must be [B,Hkv,S,D]")
-    Hkv = k.shape[1]
+    B, Hq, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError("q is [B,Hq,Sq,D]; k and v must be [B,Hkv,Skv,D]")
+    Hkv, Skv = k.shape[1], k.shape[2]
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
-    return B, Hq, Hkv, S, D
+    return B, Hq, Hkv, Sq, Skv, D
 
 
-def sdpa_forward(q, k, v, scale, causal, heads=None, row_block=512):
-    """O [B,Hq,S,D] and L [B,Hq,S] in fp64.
+def sdpa_forward(q, k, v, scale, causal, heads=None, row_block=512, window=None):
+    """O [B,Hq,Sq,D] and L [B,Hq,Sq] in fp64 (keys may be longer or shorter: Skv).
 
     ``heads``: optional list of (b, h) to compute; other heads are left NaN.
+    ``window``: optional left window (see ``visible``).
     """
-    B, Hq, Hkv, S, D = _check_shapes(q, k, v)
-    O = np.full((B, Hq, S, D), np.nan)
-    L = np.full((B, Hq, S), np.nan)
+    B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
+    off = Skv - Sq
+    O = np.full((B, Hq, Sq, D), np.nan)
+    L = np.full((B, Hq, Sq), np.nan)
     todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
     for b, h in todo:
         g = _kv_head(h, Hq, Hkv)
         kh, vh = _f64(k[b, g]), _f64(v[b, g])
-        for r0 in range(0, S, row_block):
-            r1 = min(S, r0 + row_block)
+        for r0 in range(0, Sq, row_block):
+            r1 = min(Sq, r0 + row_block)
             rows = np.arange(r0, r1)
-            P, Lr, nc = softmax_probs(q[b, h, r0:r1], rows, kh, scale, causal)
+            P, Lr, nc = softmax_probs(q[b, h, r0:r1], rows, kh, scale, causal, off, window)
             O[b, h, r0:r1] = P @ vh[:nc]
             L[b, h, r0:r1] = Lr
     return O, L
 
 
-def sdpa_forward_rows(q, k, v, scale, causal, b, h, rows):
+def sdpa_forward_rows(q, k, v, scale, causal, b, h, rows, window=None):
     """O and L of selected rows of one (b, h): ((n, D), (n,)) in fp64."""
-    B, Hq, Hkv, S, D = _check_shapes(q, k, v)
+    B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
     g = _kv_head(h, Hq, Hkv)
     rows = np.asarray(rows, dtype=np.int64)
-    P, Lr, nc = softmax_probs(q[b, h][rows], rows, k[b, g], scale, causal)
+    P, Lr, nc = softmax_probs(q[b, h][rows], rows, k[b, g], scale, causal, Skv - Sq, window)
     return P @ _f64(v[b, g][:nc]), Lr
 
 
-def _row_block_backward(q_blk, rows, do_blk, kh, vh, scale, causal):
-    P, Lr, nc = softmax_probs(q_blk, rows, kh, scale, causal)
+def _row_block_backward(q_blk, rows, do_blk, kh, vh, scale, causal, off=0, window=None):
+    P, Lr, nc = softmax_probs(q_blk, rows, kh, scale, causal, off, window)
     do_blk = _f64(do_blk)
     O = P @ vh[:nc]
     dP = do_blk @ vh[:nc].T
@@ -117,34 +149,36 @@ def _row_block_backward(q_blk, rows, do_blk, kh, vh, scale, causal):
     return P, Lr, nc, O, dS
 
 
-def sdpa_backward(q, k, v, do, scale, causal, groups=None, row_block=512):
+def sdpa_backward(q, k, v, do, scale, causal, groups=None, row_block=512, window=None):
     """Gradients of sum(dO * O) with respect to q, k, v (fp64), plus O and L.
 
     ``groups``: optional list of (b, g) KV heads to compute; the query heads
     reading them are computed in full and everything else is left NaN.
-    Returns a dict with keys o, lse, dq, dk, dv.
+    Keys may be longer or shorter than queries (Skv); ``window`` as in
+    ``visible``.  Returns a dict with keys o, lse, dq, dk, dv.
     """
-    B, Hq, Hkv, S, D = _check_shapes(q, k, v)
+    B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
+    off = Skv - Sq
     G = Hq // Hkv
     out = {
-        "o": np.full((B, Hq, S, D), np.nan),
-        "lse": np.full((B, Hq, S), np.nan),
-        "dq": np.full((B, Hq, S, D), np.nan),
-        "dk": np.full((B, Hkv, S, D), np.nan),
-        "dv": np.full((B, Hkv, S, D), np.nan),
+        "o": np.full((B, Hq, Sq, D), np.nan),
+        "lse": np.full((B, Hq, Sq), np.nan),
+        "dq": np.full((B, Hq, Sq, D), np.nan),
+        "dk": np.full((B, Hkv, Skv, D), np.nan),
+        "dv": np.full((B, Hkv, Skv, D), np.nan),
     }
     todo = groups if groups is not None else [(b, g) for b in range(B) for g in range(Hkv)]
     for b, g in todo:
         kh, vh = _f64(k[b, g]), _f64(v[b, g])
-        dk = np.zeros((S, D))
-        dv = np.zeros((S, D))
+        dk = np.zeros((Skv, D))
+        dv = np.zeros((Skv, D))
         for h in range(g * G, (g + 1) * G):
             qh = _f64(q[b, h])
-            for r0 in range(0, S, row_block):
-                r1 = min(S, r0 + row_block)
+            for r0 in range(0, Sq, row_block):
+                r1 = min(Sq, r0 + row_block)
                 rows = np.arange(r0, r1)
                 P, Lr, nc, O, dS = _row_block_backward(
-                    qh[r0:r1], rows, do[b, h, r0:r1], kh, vh, scale, causal)
+                    qh[r0:r1], rows, do[b, h, r0:r1], kh, vh, scale, causal, off, window)
                 out["o"][b, h, r0:r1] = O
                 out["lse"][b, h, r0:r1] = Lr
                 out["dq"][b, h, r0:r1] = scale * (dS @ kh[:nc])
@@ -155,11 +189,48 @@ def sdpa_backward(q, k, v, do, scale, causal, groups=None, row_block=512):
     return out
 
 
-def sdpa_dq_rows(q, k, v, do, scale, causal, b, h, rows):
+def sdpa_dq_rows(q, k, v, do, scale, causal, b, h, rows, window=None):
     """dQ of selected rows of one (b, h), (n, D) in fp64 (each row needs only its own P and dP)."""
-    B, Hq, Hkv, S, D = _check_shapes(q, k, v)
+    B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
     g = _kv_head(h, Hq, Hkv)
     rows = np.asarray(rows, dtype=np.int64)
     kh, vh = _f64(k[b, g]), _f64(v[b, g])
-    _, _, nc, _, dS = _row_block_backward(q[b, h][rows], rows, do[b, h][rows], kh, vh, scale, causal)
+    _, _, nc, _, dS = _row_block_backward(q[b, h][rows], rows, do[b, h][rows], kh, vh, scale, causal,
+                                          Skv - Sq, window)
     return scale * (dS @ kh[:nc])
+
+
+def _seq_slices(cu):
+    cu = np.asarray(cu, dtype=np.int64)
+    return [(int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)]
+
+
+def sdpa_forward_varlen(q, k, v, cu_q, cu_k, scale, causal, window=None):
+    """Packed variable-length batch: q [Hq, Tq, D], k, v [Hkv, Tk, D]; sequence b owns
+    query rows cu_q[b]:cu_q[b+1] and keys cu_k[b]:cu_k[b+1] and is attended on its
+    own (its offset is its own key length minus its own query length).
+    Returns O [Hq, Tq, D], L [Hq, Tq]."""
+    Hq, Tq, D = q.shape
+    O = np.zeros((Hq, Tq, D))
+    L = np.full((Hq, Tq), np.nan)
+    for (q0, q1), (k0, k1) in zip(_seq_slices(cu_q), _seq_slices(cu_k)):
+        if q1 == q0:
+            continue
+        Ob, Lb = sdpa_forward(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], scale, causal,
+                              window=window)
+        O[:, q0:q1], L[:, q0:q1] = Ob[0], Lb[0]
+    return O, L
+
+
+def sdpa_backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal, window=None):
+    """Packed variable-length backward (layouts as ``sdpa_forward_varlen``); dict o, lse, dq, dk, dv."""
+    out = {"o": np.zeros(q.shape), "lse": np.full(q.shape[:2], np.nan), "dq": np.zeros(q.shape),
+           "dk": np.zeros(k.shape), "dv": np.zeros(v.shape)}
+    for (q0, q1), (k0, k1) in zip(_seq_slices(cu_q), _seq_slices(cu_k)):
+        if q1 == q0:
+            continue
+        g = sdpa_backward(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], do[None, :, q0:q1],
+                          scale, causal, window=window)
+        out["o"][:, q0:q1], out["lse"][:, q0:q1], out["dq"][:, q0:q1] = g["o"][0], g["lse"][0], g["dq"][0]
+        out["dk"][:, k0:k1], out["dv"][:, k0:k1] = g["dk"][0], g["dv"][0]
+    return out

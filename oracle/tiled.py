@@ -54,40 +54,51 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _mask(s, q_pos, k_pos, causal, S):
-    bad = k_pos[None, :] >= S
+def _mask(s, q_pos, k_pos, causal, Skv, off=0, window=None):
+    bad = k_pos[None, :] >= Skv
     if causal:
-        bad = bad | (k_pos[None, :] > q_pos[:, None])
+        bad = bad | (k_pos[None, :] > q_pos[:, None] + off)
+    if window is not None:
+        bad = bad | (k_pos[None, :] < q_pos[:, None] + off - window)
     return np.where(bad, -np.inf, s)
 
 
-def online_forward(q, k, v, scale, causal, br=64, bc=64, return_state=False):
-    """Returns O [B,Hq,S,D], L [B,Hq,S] (fp64); with ``return_state`` also (m, l, acc)."""
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+def online_forward(q, k, v, scale, causal, br=64, bc=64, return_state=False, window=None):
+    """Returns O [B,Hq,Sq,D], L [B,Hq,Sq] (fp64); with ``return_state`` also (m, l, acc).
+
+    Keys may be longer or shorter than the queries (Skv); the causal diagonal is
+    aligned bottom-right, offset = Skv - Sq ("Phase 14", section Causal Mask:
+    kv_offset).  ``window`` (>= 0) also hides keys before i + offset - window; KV
+    tiles wholly before a Q tile's window are never visited either.  A row that
+    sees no key ends with l = 0: its output is 0 and its L is -inf.
+    """
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    off = Skv - Sq
     G = Hq // Hkv
-    O = np.zeros((B, Hq, S, D))
-    L = np.zeros((B, Hq, S))
-    M = np.zeros((B, Hq, S))
-    ELL = np.zeros((B, Hq, S))
-    ACC = np.zeros((B, Hq, S, D))
+    O = np.zeros((B, Hq, Sq, D))
+    L = np.zeros((B, Hq, Sq))
+    M = np.zeros((B, Hq, Sq))
+    ELL = np.zeros((B, Hq, Sq))
+    ACC = np.zeros((B, Hq, Sq, D))
     for b in range(B):
         for h in range(Hq):
             g = h // G
             Kh, Vh = _f64(k[b, g]), _f64(v[b, g])
-            for i0 in range(0, S, br):
-                i1 = min(i0 + br, S)
+            for i0 in range(0, Sq, br):
+                i1 = min(i0 + br, Sq)
                 Qi = _f64(q[b, h, i0:i1])
                 q_pos = np.arange(i0, i1)
                 m = np.full(i1 - i0, -np.inf)
                 ell = np.zeros(i1 - i0)
                 acc = np.zeros((i1 - i0, D))
-                for j0 in range(0, S, bc):
-                    if causal and j0 > i1 - 1:
+                first = 0 if window is None else max(0, i0 + off - window) // bc * bc
+                for j0 in range(first, Skv, bc):
+                    if causal and j0 > i1 - 1 + off:
                         break                                   # tile-level causal skip
-                    j1 = min(j0 + bc, S)
+                    j1 = min(j0 + bc, Skv)
                     s = scale * (Qi @ Kh[j0:j1].T)
-                    s = _mask(s, q_pos, np.arange(j0, j1), causal, S)
+                    s = _mask(s, q_pos, np.arange(j0, j1), causal, Skv, off, window)
                     m_new = np.maximum(m, s.max(axis=1))
                     ref = np.where(np.isneginf(m_new), 0.0, m_new)
                     alpha = np.exp(m - ref)
@@ -95,42 +106,51 @@ def online_forward(q, k, v, scale, causal, br=64, bc=64, return_state=False):
                     ell = ell * alpha + p.sum(axis=1)
                     acc = acc * alpha[:, None] + p @ Vh[j0:j1]
                     m = m_new
-                O[b, h, i0:i1] = acc / ell[:, None]
-                L[b, h, i0:i1] = m + np.log(ell)
+                seen = ell > 0
+                O[b, h, i0:i1] = np.where(seen[:, None], acc / np.where(seen, ell, 1.0)[:, None], 0.0)
+                with np.errstate(divide="ignore"):
+                    L[b, h, i0:i1] = np.where(seen, m + np.log(np.where(seen, ell, 1.0)), -np.inf)
                 M[b, h, i0:i1], ELL[b, h, i0:i1], ACC[b, h, i0:i1] = m, ell, acc
     if return_state:
         return O, L, (M, ELL, ACC)
     return O, L
 
 
-def online_backward(q, k, v, o, lse, do, scale, causal, br=64, bc=64):
-    """dQ [B,Hq,S,D], dK, dV [B,Hkv,S,D] (fp64) from the forward's O and L."""
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+def online_backward(q, k, v, o, lse, do, scale, causal, br=64, bc=64, window=None):
+    """dQ [B,Hq,Sq,D], dK, dV [B,Hkv,Skv,D] (fp64) from the forward's O and L.
+
+    Masks as in ``online_forward``; for a KV tile only the Q tiles that can see
+    one of its keys are visited (from the first row at or after j0 - offset, to
+    the last row whose window still reaches the tile's last key)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    off = Skv - Sq
     G = Hq // Hkv
     o, lse, do = _f64(o), _f64(lse), _f64(do)
     Dvec = (do * o).sum(axis=-1)                               # first pass: D = rowsum(dO * O)
-    dQ = np.zeros((B, Hq, S, D))
-    dK = np.zeros((B, Hkv, S, D))
-    dV = np.zeros((B, Hkv, S, D))
+    dQ = np.zeros((B, Hq, Sq, D))
+    dK = np.zeros((B, Hkv, Skv, D))
+    dV = np.zeros((B, Hkv, Skv, D))
     for b in range(B):
         for g in range(Hkv):
             Kh, Vh = _f64(k[b, g]), _f64(v[b, g])
-            for j0 in range(0, S, bc):
-                j1 = min(j0 + bc, S)
+            for j0 in range(0, Skv, bc):
+                j1 = min(j0 + bc, Skv)
                 k_pos = np.arange(j0, j1)
                 Kj, Vj = Kh[j0:j1], Vh[j0:j1]
                 dKj = np.zeros((j1 - j0, D))
                 dVj = np.zeros((j1 - j0, D))
                 for h in range(g * G, (g + 1) * G):
-                    first = (j0 // br) * br if causal else 0
-                    for i0 in range(first, S, br):
-                        i1 = min(i0 + br, S)
+                    first = (max(0, j0 - off) // br) * br if causal else 0
+                    last = Sq if window is None else min(Sq, j1 - 1 - off + window + 1)
+                    for i0 in range(first, last, br):
+                        i1 = min(i0 + br, Sq)
                         Qi = _f64(q[b, h, i0:i1])
                         dOi = do[b, h, i0:i1]
                         s = scale * (Qi @ Kj.T)
-                        s = _mask(s, np.arange(i0, i1), k_pos, causal, S)
-                        p = np.where(np.isfinite(s), np.exp(s - lse[b, h, i0:i1, None]), 0.0)
+                        s = _mask(s, np.arange(i0, i1), k_pos, causal, Skv, off, window)
+                        with np.errstate(invalid="ignore"):
+                            p = np.where(np.isfinite(s), np.exp(s - lse[b, h, i0:i1, None]), 0.0)
                         dVj += p.T @ dOi
                         dp = dOi @ Vj.T
                         ds = p * (dp - Dvec[b, h, i0:i1, None])

@@ -377,3 +377,163 @@ def test_workload_inputs_are_on_the_dtype_grid():
         assert np.array_equal(a.astype(np.float16).astype(np.float32), a)
     z = make_inputs(1, 2, 1, 8, 4, "bf16", seed=0)
     assert all(np.array_equal(x[key], z[key]) for key in x)
+
+
+# ---------------------------------------------------------------- cross-length causal, windows, varlen
+
+def _torch_masked(q, k, v, do, scale, causal, window):
+    """PyTorch fp64 attention with the same visibility mask written as a boolean matrix."""
+    Sq, Skv = q.shape[2], k.shape[2]
+    G = q.shape[1] // k.shape[1]
+    i, j = np.arange(Sq)[:, None], np.arange(Skv)[None, :]
+    vis = np.ones((Sq, Skv), bool)
+    if causal:
+        vis &= j <= i + Skv - Sq
+    if window is not None:
+        vis &= j >= i + Skv - Sq - window
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(G, 1), tv.repeat_interleave(G, 1),
+                                         attn_mask=torch.tensor(vis), scale=scale)
+    seen = vis.any(axis=1)
+    out.backward(torch.tensor(np.where(seen[None, None, :, None], do, 0.0)))
+    return vis, out.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+MASK_CASES = [  # Sq, Skv, causal, window
+    (9, 21, True, None), (21, 9, True, None), (17, 17, True, 5), (12, 30, True, 0),
+    (30, 12, False, 4), (16, 16, False, None), (7, 40, True, 11), (25, 25, True, 30),
+]
+
+
+@pytest.mark.parametrize("Sq,Skv,causal,window", MASK_CASES)
+def test_masks_against_torch_fp64(Sq, Skv, causal, window):
+    r = np.random.default_rng(Sq * 100 + Skv)
+    q = r.standard_normal((2, 4, Sq, 8)) * 1.5
+    k, v = r.standard_normal((2, 2, Skv, 8)), r.standard_normal((2, 2, Skv, 8))
+    do = r.standard_normal((2, 4, Sq, 8))
+    scale = 0.4
+    vis, O, dq, dk, dv = _torch_masked(q, k, v, do, scale, causal, window)
+    seen = vis.any(axis=1)
+    g = oracle.sdpa_backward(q, k, v, np.where(seen[None, None, :, None], do, 0.0), scale, causal, window=window)
+    np.testing.assert_allclose(g["o"][:, :, seen], O[:, :, seen], atol=1e-12)
+    np.testing.assert_allclose(g["dq"], dq, atol=1e-12)
+    np.testing.assert_allclose(g["dk"], dk, atol=1e-12)
+    np.testing.assert_allclose(g["dv"], dv, atol=1e-12)
+    # rows that see no key: empty softmax, O = 0, L = -inf, no gradient
+    assert np.all(g["o"][:, :, ~seen] == 0) and np.all(np.isneginf(g["lse"][:, :, ~seen]))
+    g2 = oracle.sdpa_backward(q, k, v, do, scale, causal, window=window)
+    assert np.all(g2["dq"][:, :, ~seen] == 0)
+
+
+@pytest.mark.parametrize("Sq,Skv,causal,window", MASK_CASES)
+@pytest.mark.parametrize("br,bc", [(1, 1), (4, 3), (16, 8), (64, 64)])
+def test_masks_tiled_equals_dense(Sq, Skv, causal, window, br, bc):
+    q, k, v, do = rand_qkvdo(1, 2, 1, max(Sq, Skv), 4, seed=Sq + Skv + br, std=2.0)
+    q, do = q[:, :, :Sq], do[:, :, :Sq]
+    k, v = k[:, :, :Skv], v[:, :, :Skv]
+    g = oracle.sdpa_backward(q, k, v, do, 0.5, causal, window=window)
+    O, L = oracle.online_forward(q, k, v, 0.5, causal, br, bc, window=window)
+    np.testing.assert_allclose(O, g["o"], atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(L), np.isneginf(g["lse"]))
+    fin = np.isfinite(g["lse"])
+    np.testing.assert_allclose(L[fin], g["lse"][fin], atol=1e-12)
+    dq, dk, dv = oracle.online_backward(q, k, v, O, L, do, 0.5, causal, br, bc, window=window)
+    np.testing.assert_allclose(dq, g["dq"], atol=1e-12)
+    np.testing.assert_allclose(dk, g["dk"], atol=1e-12)
+    np.testing.assert_allclose(dv, g["dv"], atol=1e-12)
+
+
+def test_masks_brute_force():
+    r = np.random.default_rng(5)
+    Sq, Skv, D, scale, win = 5, 8, 3, 0.7, 2
+    q, k, v, do = (r.standard_normal(s) for s in ((1, 1, Sq, D), (1, 1, Skv, D), (1, 1, Skv, D), (1, 1, Sq, D)))
+    off = Skv - Sq
+    g = oracle.sdpa_backward(q, k, v, do, scale, True, window=win)
+    for i in range(Sq):
+        js = [j for j in range(Skv) if i + off - win <= j <= i + off]
+        s = {j: scale * sum(q[0, 0, i, d] * k[0, 0, j, d] for d in range(D)) for j in js}
+        z = sum(math.exp(x) for x in s.values())
+        for d in range(D):
+            o = sum(math.exp(s[j]) / z * v[0, 0, j, d] for j in js)
+            assert abs(g["o"][0, 0, i, d] - o) < 1e-13
+        assert abs(g["lse"][0, 0, i] - math.log(z)) < 1e-13
+
+
+def test_window_zero_sees_one_key():
+    """window = 0 under the causal mask: query i sees exactly key i + offset."""
+    q, k, v, do = rand_qkvdo(1, 2, 2, 30, 8, seed=41)
+    q, do = q[:, :, :12], do[:, :, :12]
+    off = 30 - 12
+    g = oracle.sdpa_backward(q, k, v, do, 0.3, True, window=0)
+    np.testing.assert_array_equal(g["o"], v[:, :, off:])
+    np.testing.assert_allclose(g["lse"], 0.3 * (q * k[:, :, off:]).sum(-1), atol=1e-14)
+    assert np.all(g["dq"] == 0) and np.all(g["dk"] == 0)
+    np.testing.assert_array_equal(g["dv"][:, :, off:], do)
+    assert np.all(g["dv"][:, :, :off] == 0)
+
+
+def test_single_query_is_full_attention():
+    """One query row with the bottom-right causal mask sees every key (a decode step)."""
+    q, k, v, do = rand_qkvdo(2, 4, 2, 50, 8, seed=42)
+    q1, do1 = q[:, :, -1:], do[:, :, -1:]
+    a = oracle.sdpa_backward(q1, k, v, do1, 0.35, True)
+    b = oracle.sdpa_backward(q1, k, v, do1, 0.35, False)
+    for key in ("o", "lse", "dq", "dk", "dv"):
+        np.testing.assert_allclose(a[key], b[key], atol=1e-14)
+
+
+def test_varlen_equal_lengths_match_dense_batch():
+    r = np.random.default_rng(43)
+    B, Hq, Hkv, Sq, Skv, D = 3, 4, 2, 11, 17, 8
+    q, do = r.standard_normal((B, Hq, Sq, D)), r.standard_normal((B, Hq, Sq, D))
+    k, v = r.standard_normal((B, Hkv, Skv, D)), r.standard_normal((B, Hkv, Skv, D))
+    dense = oracle.sdpa_backward(q, k, v, do, 0.4, True, window=6)
+    pack = lambda x: np.concatenate([x[b] for b in range(B)], axis=1)      # [H, B*S, D]
+    cu_q, cu_k = np.arange(B + 1) * Sq, np.arange(B + 1) * Skv
+    vl = oracle.sdpa_backward_varlen(pack(q), pack(k), pack(v), pack(do), cu_q, cu_k, 0.4, True, window=6)
+    for key in ("o", "dq", "dk", "dv"):
+        np.testing.assert_allclose(vl[key], pack(dense[key]), atol=1e-13)
+    np.testing.assert_allclose(vl["lse"], np.concatenate([dense["lse"][b] for b in range(B)], axis=1), atol=1e-13)
+    O, L = oracle.sdpa_forward_varlen(pack(q), pack(k), pack(v), cu_q, cu_k, 0.4, True, window=6)
+    np.testing.assert_allclose(O, vl["o"], atol=1e-14)
+
+
+def test_varlen_ragged_brute_force():
+    r = np.random.default_rng(44)
+    lq, lk = [3, 0, 5, 1], [4, 2, 5, 6]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q, k, v = r.standard_normal((2, cu_q[-1], 2)), r.standard_normal((1, cu_k[-1], 2)), r.standard_normal((1, cu_k[-1], 2))
+    O, L = oracle.sdpa_forward_varlen(q, k, v, cu_q, cu_k, 0.9, True)
+    for b in range(4):
+        off = lk[b] - lq[b]
+        for h in range(2):
+            for i in range(lq[b]):
+                js = [j for j in range(lk[b]) if j <= i + off]
+                s = [0.9 * float(q[h, cu_q[b] + i] @ k[0, cu_k[b] + j]) for j in js]
+                w = np.exp(np.array(s) - max(s))
+                ref = (w[:, None] * v[0, [cu_k[b] + j for j in js]]).sum(0) / w.sum()
+                np.testing.assert_allclose(O[h, cu_q[b] + i], ref, atol=1e-13)
+
+
+@pytest.mark.parametrize("Sq,Skv,window", [(4, 7, 2), (6, 3, None), (5, 5, 1)])
+def test_masks_finite_differences(Sq, Skv, window):
+    r = np.random.default_rng(Sq * 10 + Skv)
+    q, k, v = r.standard_normal((1, 2, Sq, 4)), r.standard_normal((1, 1, Skv, 4)), r.standard_normal((1, 1, Skv, 4))
+    do = r.standard_normal((1, 2, Sq, 4))
+
+    def f(q_, k_, v_):
+        return float((oracle.sdpa_forward(q_, k_, v_, 0.5, True, window=window)[0] * do).sum())
+
+    g = oracle.sdpa_backward(q, k, v, do, 0.5, True, window=window)
+    h = 1e-6
+    for name, arr in (("dq", q), ("dk", k), ("dv", v)):
+        for ix in np.ndindex(arr.shape):
+            if r.random() > 0.3:
+                continue
+            p, m = arr.copy(), arr.copy()
+            p[ix] += h
+            m[ix] -= h
+            a = {"dq": (p, k, v), "dk": (q, p, v), "dv": (q, k, p)}[name]
+            b = {"dq": (m, k, v), "dk": (q, m, v), "dv": (q, k, m)}[name]
+            fd = (f(*a) - f(*b)) / (2 * h)
+            assert abs(g[name][ix] - fd) <= 1e-7 * max(1.0, abs(fd)), (name, ix)

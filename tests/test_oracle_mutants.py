@@ -57,6 +57,26 @@ def _pins_hold(dense, tiled):
     ok &= np.allclose(dqr, ref["dq"][0, 3], atol=1e-10)
     ok &= np.allclose(O, ref["o"], atol=1e-10) and np.allclose(L, g["lse"], atol=1e-10)
     ok &= all(np.allclose(a, ref[n], atol=1e-10) for a, n in zip((dq, dk, dv), ("dq", "dk", "dv")))
+    # longer keys (bottom-right causal alignment) with a sliding window, against an explicit mask
+    Sq, Skv, win = 13, 19, 4
+    q2, k2, v2, do2 = q[:, :, :Sq], rng.standard_normal((B, Hkv, Skv, D)), rng.standard_normal((B, Hkv, Skv, D)), do[:, :, :Sq]
+    i, j = np.arange(Sq)[:, None], np.arange(Skv)[None, :]
+    mask = torch.tensor((j <= i + Skv - Sq) & (j >= i + Skv - Sq - win))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q2, k2, v2))
+    out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(2, 1), tv.repeat_interleave(2, 1),
+                                         attn_mask=mask, scale=scale)
+    out.backward(torch.tensor(do2))
+    ref2 = {"o": out.detach().numpy(), "dq": tq.grad.numpy(), "dk": tk.grad.numpy(), "dv": tv.grad.numpy()}
+    try:
+        with np.errstate(all="ignore"):
+            g2 = dense.sdpa_backward(q2, k2, v2, do2, scale, True, window=win)
+            O2, L2 = tiled.online_forward(q2, k2, v2, scale, True, 4, 3, window=win)
+            t2 = tiled.online_backward(q2, k2, v2, O2, L2, do2, scale, True, 4, 3, window=win)
+    except Exception:
+        return False
+    ok &= all(np.allclose(g2[n], ref2[n], atol=1e-10) for n in ref2)
+    ok &= np.allclose(O2, ref2["o"], atol=1e-10) and np.allclose(L2, g2["lse"], atol=1e-10)
+    ok &= all(np.allclose(a, ref2[n], atol=1e-10) for a, n in zip(t2, ("dq", "dk", "dv")))
     return bool(ok)
 
 
@@ -66,9 +86,11 @@ def test_unmutated_oracle_passes():
 
 DENSE_MUTANTS = [
     ("sc = scale * (q_rows @ k_head[:ncols].T)", "sc = (q_rows @ k_head[:ncols].T)"),
-    ("> rows[:, None], -np.inf", ">= rows[:, None], -np.inf"),
+    ("vis &= j <= i + offset", "vis &= j < i + offset"),
     ("e = np.exp(sc - m)", "e = np.exp(sc)"),
-    ("(m + np.log(z))[:, 0]", "(np.log(z))[:, 0]"),
+    ("(m + np.log(np.where(z > 0, z, 1.0)))[:, 0]", "(np.log(np.where(z > 0, z, 1.0)))[:, 0]"),
+    ("vis &= j >= i + offset - window", "vis &= j > i + offset - window"),
+    ("return h // (Hq // Hkv)", "return h % Hkv"),
     ("dP - (P * dP).sum(axis=1, keepdims=True)", "dP + (P * dP).sum(axis=1, keepdims=True)"),
     ("dP = do_blk @ vh[:nc].T", "dP = do_blk @ vh[:nc].T * 0.5"),
     ('out["dq"][b, h, r0:r1] = scale * (dS @ kh[:nc])', 'out["dq"][b, h, r0:r1] = (dS @ kh[:nc])'),
@@ -80,14 +102,16 @@ DENSE_MUTANTS = [
 TILED_MUTANTS = [
     ("ell = ell * alpha + p.sum(axis=1)", "ell = ell + p.sum(axis=1)"),
     ("acc = acc * alpha[:, None] + p @ Vh[j0:j1]", "acc = acc + p @ Vh[j0:j1]"),
-    ("if causal and j0 > i1 - 1:", "if causal and j0 > i0:"),
-    ("L[b, h, i0:i1] = m + np.log(ell)", "L[b, h, i0:i1] = np.log(ell)"),
-    ("bad = bad | (k_pos[None, :] > q_pos[:, None])", "bad = bad | (k_pos[None, :] >= q_pos[:, None])"),
+    ("if causal and j0 > i1 - 1 + off:", "if causal and j0 > i0 + off:"),
+    ("bad = bad | (k_pos[None, :] < q_pos[:, None] + off - window)", "bad = bad | (k_pos[None, :] <= q_pos[:, None] + off - window)"),
+    ("last = Sq if window is None else min(Sq, j1 - 1 - off + window + 1)", "last = Sq if window is None else min(Sq, j1 - 1 - off + window)"),
+    ("m + np.log(np.where(seen, ell, 1.0))", "np.log(np.where(seen, ell, 1.0))"),
+    ("bad = bad | (k_pos[None, :] > q_pos[:, None] + off)", "bad = bad | (k_pos[None, :] >= q_pos[:, None] + off)"),
     ("np.exp(s - lse[b, h, i0:i1, None])", "np.exp(s - 0 * lse[b, h, i0:i1, None])"),
     ("ds = p * (dp - Dvec[b, h, i0:i1, None])", "ds = p * (dp + Dvec[b, h, i0:i1, None])"),
     ("dQ[b, h, i0:i1] += scale * (ds @ Kj)", "dQ[b, h, i0:i1] += scale * (p @ Kj)"),
     ("dKj += scale * (ds.T @ Qi)", "dKj += (ds.T @ Qi)"),
-    ("first = (j0 // br) * br if causal else 0", "first = (j0 // br + 1) * br if causal else 0"),
+    ("first = (max(0, j0 - off) // br) * br if causal else 0", "first = (j0 // br + 1) * br if causal else 0"),
     ("Dvec = (do * o).sum(axis=-1)", "Dvec = (do * o).sum(axis=-1) * 0"),
     ("g = h // G\n            Kh, Vh", "g = h % Hkv\n            Kh, Vh"),
 ]
