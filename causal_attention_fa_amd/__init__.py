@@ -1,12 +1,15 @@
 """Python binding of libfa.so, the MI355X fused causal attention library.
 
-The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes`` and
-``fa_status_string`` mirror the C ABI in ``include/fa.h`` one to one: they take
-raw device addresses (ints) and sizes and return the C status code.  Every step
-of the computation runs in the HIP kernels behind that ABI; this module only
+The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_fwd_ex``,
+``fa_bwd_ex``, ``fa_bwd_ex_workspace_bytes`` and ``fa_status_string`` mirror
+the C ABI in ``include/fa.h`` one to one: they take raw device addresses (ints)
+and sizes (or an ``fa_params_t``) and return the C status code.  Every step of
+the computation runs in the HIP kernels behind that ABI; this module only
 marshals arguments.
 
-``forward`` / ``backward`` are conveniences for PyTorch callers: they allocate
+``forward`` / ``backward`` (dense batches, queries and keys of any lengths,
+optional sliding window) and ``forward_varlen`` / ``backward_varlen`` (packed
+variable-length batches) are conveniences for PyTorch callers: they allocate
 the outputs (and the backward workspace) with torch on the inputs' device, pass
 torch's current stream, and raise ``FAError`` on a non-OK status.
 
@@ -22,7 +25,8 @@ __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FA_F32", "FA_F16", "FA_BF16", "FAError", "library_path", "lib",
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_profile_events",
-    "forward", "backward",
+    "fa_params_t", "params", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes",
+    "forward", "backward", "forward_varlen", "backward_varlen",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
@@ -31,6 +35,25 @@ FA_F32, FA_F16, FA_BF16 = range(3)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libfa.so")
 _lib = None
+
+
+class fa_params_t(ctypes.Structure):
+    """The C struct fa_params_t (include/fa.h), field for field."""
+    _fields_ = [
+        ("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int),
+        ("Sq", ctypes.c_int), ("Skv", ctypes.c_int), ("D", ctypes.c_int),
+        ("scale", ctypes.c_float), ("causal", ctypes.c_int), ("window", ctypes.c_int),
+        ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+        ("total_q", ctypes.c_int), ("total_k", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+    ]
+
+
+def params(B, Hq, Hkv, Sq, Skv, D, scale, causal=True, window=None, dtype=FA_BF16,
+           cu_seqlens_q=None, cu_seqlens_k=None, total_q=0, total_k=0) -> fa_params_t:
+    """An fa_params_t; ``window=None`` means no window, cu_seqlens_* are device addresses."""
+    return fa_params_t(B, Hq, Hkv, Sq, Skv, D, scale, int(causal), -1 if window is None else int(window),
+                       cu_seqlens_q, cu_seqlens_k, total_q, total_k, dtype)
 
 
 class FAError(RuntimeError):
@@ -58,6 +81,13 @@ def lib() -> ctypes.CDLL:
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_profile_events.argtypes = [vp, i]
         L.fa_profile_events.restype = None
+        pp = ctypes.POINTER(fa_params_t)
+        L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, pp, vp]
+        L.fa_fwd_ex.restype = i
+        L.fa_bwd_ex_workspace_bytes.argtypes = [pp]
+        L.fa_bwd_ex_workspace_bytes.restype = sz
+        L.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp]
+        L.fa_bwd_ex.restype = i
         _lib = L
     return _lib
 
@@ -76,6 +106,23 @@ def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, S, D, scale, causal, dty
 
 def fa_bwd_workspace_bytes(B, Hq, Hkv, S, D) -> int:
     return int(lib().fa_bwd_workspace_bytes(B, Hq, Hkv, S, D))
+
+
+def _pp(p):
+    return None if p is None else ctypes.byref(p)
+
+
+def fa_fwd_ex(q, k, v, o, lse, p, stream) -> int:
+    """p: an fa_params_t (or None, which the library rejects)."""
+    return lib().fa_fwd_ex(q, k, v, o, lse, _pp(p), stream)
+
+
+def fa_bwd_ex_workspace_bytes(p) -> int:
+    return int(lib().fa_bwd_ex_workspace_bytes(_pp(p)))
+
+
+def fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, p, workspace, workspace_bytes, stream) -> int:
+    return lib().fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, _pp(p), workspace, workspace_bytes, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -102,53 +149,133 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
+def _same(ts, what):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != ts[0].dtype:
+            raise ValueError(f"{what} must be contiguous device tensors of one dtype")
+
+
 def _check(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
-        raise ValueError("q is [B,Hq,S,D]; k and v are [B,Hkv,S,D]")
-    B, Hq, S, D = q.shape
-    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != D:
-        raise ValueError("q, k, v disagree on B, S or D")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("q, k, v must be contiguous device tensors of one dtype")
-    return B, Hq, k.shape[1], S, D
+        raise ValueError("q is [B,Hq,Sq,D]; k and v are [B,Hkv,Skv,D]")
+    B, Hq, Sq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("q, k, v disagree on B or D")
+    _same((q, k, v), "q, k, v")
+    return B, Hq, k.shape[1], Sq, k.shape[2], D
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
 
 
 def _stream(t):
     return _torch().cuda.current_stream(t.device).cuda_stream
 
 
-def forward(q, k, v, scale=None, causal=True, with_lse=True):
-    """(o, lse) for device tensors q [B,Hq,S,D], k, v [B,Hkv,S,D]; lse is fp32 [B,Hq,S] or None."""
+def _scale(scale, D):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+def forward(q, k, v, scale=None, causal=True, with_lse=True, window=None):
+    """(o, lse) for device tensors q [B,Hq,Sq,D], k, v [B,Hkv,Skv,D]; lse is fp32 [B,Hq,Sq] or None.
+
+    With Sq == Skv and no window this calls fa_fwd, otherwise fa_fwd_ex (causal
+    diagonal aligned bottom-right; ``window`` keys before the diagonal stay visible)."""
     torch = _torch()
-    B, Hq, Hkv, S, D = _check(q, k, v)
-    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    B, Hq, Hkv, Sq, Skv, D = _check(q, k, v)
+    scale = _scale(scale, D)
     o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if with_lse else None
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr() if with_lse else None,
-                B, Hq, Hkv, S, D, scale, causal, _dtype_code(q), _stream(q))
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if with_lse else None
+    ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse))
+    if Sq == Skv and window is None:
+        st = fa_fwd(*ptrs, B, Hq, Hkv, Sq, D, scale, causal, _dtype_code(q), _stream(q))
+    else:
+        p = params(B, Hq, Hkv, Sq, Skv, D, scale, causal, window, _dtype_code(q))
+        st = fa_fwd_ex(*ptrs, p, _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_fwd")
     return o, lse
 
 
-def backward(q, k, v, o, lse, do, scale=None, causal=True, workspace=None):
+def _workspace(nbytes, workspace, device):
+    if workspace is None:
+        workspace = _torch().empty(max(nbytes, 256), dtype=_torch().uint8, device=device)
+    return workspace
+
+
+def backward(q, k, v, o, lse, do, scale=None, causal=True, workspace=None, window=None):
     """(dq, dk, dv) for the forward's inputs, its outputs o and lse, and dO."""
     torch = _torch()
-    B, Hq, Hkv, S, D = _check(q, k, v)
+    B, Hq, Hkv, Sq, Skv, D = _check(q, k, v)
     for t in (o, do):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError("o and dO must match q")
-    if lse.shape != (B, Hq, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous fp32 [B,Hq,S]")
-    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    nbytes = fa_bwd_workspace_bytes(B, Hq, Hkv, S, D)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [B,Hq,Sq]")
+    scale = _scale(scale, D)
+    dense = Sq == Skv and window is None
+    p = params(B, Hq, Hkv, Sq, Skv, D, scale, causal, window, _dtype_code(q))
+    workspace = _workspace(fa_bwd_ex_workspace_bytes(p), workspace, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, S, D, scale, causal,
-                _dtype_code(q), workspace.data_ptr(), workspace.numel(), _stream(q))
+    ptrs = tuple(_ptr(t) for t in (q, k, v, o, lse, do, dq, dk, dv))
+    if dense:
+        st = fa_bwd(*ptrs, B, Hq, Hkv, Sq, D, scale, causal, _dtype_code(q), workspace.data_ptr(),
+                    workspace.numel(), _stream(q))
+    else:
+        st = fa_bwd_ex(*ptrs, p, workspace.data_ptr(), workspace.numel(), _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def _check_varlen(q, k, v, cu_q, cu_k):
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("q is [Hq,total_q,D]; k and v are [Hkv,total_k,D]")
+    _same((q, k, v), "q, k, v")
+    for c in (cu_q, cu_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_cuda or not c.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous int32 device vectors")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need B + 1 entries each")
+    return cu_q.numel() - 1, q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2]
+
+
+def _varlen_params(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal, window):
+    B, Hq, Hkv, Tq, Tk, D = _check_varlen(q, k, v, cu_q, cu_k)
+    return params(B, Hq, Hkv, int(max_q), int(max_k), D, _scale(scale, D), causal, window, _dtype_code(q),
+                  cu_q.data_ptr(), cu_k.data_ptr(), Tq, Tk)
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None, causal=True,
+                   window=None):
+    """Packed batch: q [Hq,total_q,D], k, v [Hkv,total_k,D], cu_seqlens_* int32 [B+1] on the device.
+    Returns o [Hq,total_q,D] and lse fp32 [Hq,total_q]; max_seqlen_* bound the per-sequence lengths."""
+    torch = _torch()
+    p = _varlen_params(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, window)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    st = fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), p, _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_ex")
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
+                    causal=True, window=None, workspace=None):
+    """(dq, dk, dv) of a packed batch (layouts as ``forward_varlen``)."""
+    torch = _torch()
+    p = _varlen_params(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, window)
+    for t in (o, do):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("o and dO must match q")
+    if lse.shape != q.shape[:2] or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous fp32 [Hq,total_q]")
+    workspace = _workspace(fa_bwd_ex_workspace_bytes(p), workspace, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = fa_bwd_ex(*(_ptr(t) for t in (q, k, v, o, lse, do, dq, dk, dv)), p, workspace.data_ptr(),
+                   workspace.numel(), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_ex")
     return dq, dk, dv

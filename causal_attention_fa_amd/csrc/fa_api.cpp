@@ -3,6 +3,7 @@
 // the GPU before every argument has been checked.
 #include "../../include/fa.h"
 
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -11,29 +12,71 @@
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-// Shared shape / scalar checks of fa_fwd and fa_bwd.  Returns FA_OK and sets
-// *empty when there is nothing to compute.
-fa_status_t check_problem(int B, int Hq, int Hkv, int S, int D, float scale, fa_dtype_t dtype, bool* empty) {
-  *empty = false;
-  if (B < 0 || Hq < 0 || Hkv < 0 || S < 0 || D < 0) return FA_ERR_INVALID_ARG;
-  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if ((long long)B * Hq * S == 0) {
-    if (Hkv > 0 && Hq > 0 && Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-    *empty = true;
-    return FA_OK;
-  }
-  if (Hkv == 0 || Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  if (!(scale > 0.f)) return FA_ERR_UNSUPPORTED;
-  return FA_OK;
-}
+// A required buffer: non-NULL and 16-byte aligned.
+bool present(const void* p) { return p != nullptr && aligned16(p); }
+
+constexpr int kMaxLen = 1 << 29;  // longest query or key sequence (keeps i + offset +- window in int)
 
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
 thread_local hipEvent_t* g_events = nullptr;
 thread_local int g_nevents = 0;
+
+// Checks an extended problem; on FA_OK fills the kernel-side description and
+// the number of query rows and key rows (over all heads).
+fa_status_t check(const fa_params_t* p, fa::Problem* pb, long long* qrows, long long* krows) {
+  if (p == nullptr) return FA_ERR_INVALID_ARG;
+  if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->Sq < 0 || p->Skv < 0 || p->D < 0) return FA_ERR_INVALID_ARG;
+  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (!isfinite(p->scale)) return FA_ERR_INVALID_ARG;
+  const bool packed = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
+  if (packed) {
+    if (p->cu_seqlens_q == nullptr || p->cu_seqlens_k == nullptr) return FA_ERR_INVALID_ARG;
+    if (!aligned4(p->cu_seqlens_q) || !aligned4(p->cu_seqlens_k)) return FA_ERR_INVALID_ARG;
+    if (p->total_q < 0 || p->total_k < 0) return FA_ERR_INVALID_ARG;
+    *qrows = (long long)p->Hq * p->total_q;
+    *krows = (long long)p->Hkv * p->total_k;
+  } else {
+    *qrows = (long long)p->B * p->Hq * p->Sq;
+    *krows = (long long)p->B * p->Hkv * p->Skv;
+  }
+  if (*qrows == 0 && *krows == 0) {
+    if (p->Hkv > 0 && p->Hq > 0 && p->Hq % p->Hkv != 0) return FA_ERR_INVALID_ARG;
+  } else {
+    if (p->B == 0 || p->Hq == 0 || p->Hkv == 0 || p->Hq % p->Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (p->D != 64 && p->D != 128) return FA_ERR_UNSUPPORTED;
+    if (!(p->scale > 0.f)) return FA_ERR_UNSUPPORTED;
+    // the kernels index rows and workgroups with 32-bit ints
+    if (p->Sq > kMaxLen || p->Skv > kMaxLen) return FA_ERR_UNSUPPORTED;
+    if ((long long)(p->Sq / 128 + 1) * p->B * p->Hq > INT_MAX ||
+        (long long)(p->Skv / 128 + 1) * p->B * p->Hkv > INT_MAX)
+      return FA_ERR_UNSUPPORTED;
+  }
+  // a window of Skv or more keys hides nothing (i + offset - window < 0 for
+  // every query), so it is the same problem without a window
+  const int window = (p->window < 0 || p->window >= p->Skv) ? -1 : p->window;
+  *pb = fa::Problem{p->B,       p->Hq,  p->Hkv, p->Sq, p->Skv, p->causal ? 1 : 0, window,
+                    packed ? p->cu_seqlens_q : nullptr, packed ? p->cu_seqlens_k : nullptr,
+                    packed ? p->total_q : 0, packed ? p->total_k : 0};
+  return FA_OK;
+}
+
+fa_params_t dense(int B, int Hq, int Hkv, int S, int D, float scale, int causal, fa_dtype_t dtype) {
+  fa_params_t p{};
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = S;
+  p.Skv = S;
+  p.D = D;
+  p.scale = scale;
+  p.causal = causal;
+  p.window = -1;
+  p.dtype = dtype;
+  return p;
+}
 
 }  // namespace
 
@@ -55,37 +98,59 @@ const char* fa_status_string(fa_status_t s) {
   return "FA_ERR_UNKNOWN";
 }
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,
-                   int D, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
-  bool empty = false;
-  fa_status_t st = check_problem(B, Hq, Hkv, S, D, scale, dtype, &empty);
-  if (st != FA_OK || empty) return st;
-  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
-    return FA_ERR_INVALID_ARG;
-  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, S, D, scale, causal ? 1 : 0, (int)dtype, g_events, g_nevents};
+fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, const fa_params_t* p,
+                      hipStream_t stream) {
+  fa::Problem pb;
+  long long qrows = 0, krows = 0;
+  fa_status_t st = check(p, &pb, &qrows, &krows);
+  if (st != FA_OK || qrows == 0) return st;
+  if (!present(q) || !present(o) || (lse && !aligned16(lse))) return FA_ERR_INVALID_ARG;
+  if (krows > 0 && (!present(k) || !present(v))) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{q, k, v, o, lse, pb, p->D, p->scale, (int)p->dtype, g_events, g_nevents};
   return fa::launch_fwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_ex_workspace_bytes(const fa_params_t* p) {
+  fa::Problem pb;
+  long long qrows = 0, krows = 0;
+  if (check(p, &pb, &qrows, &krows) != FA_OK) return 0;
+  return qrows > 0 ? round256((size_t)qrows * sizeof(float)) : 0;
+}
+
+fa_status_t fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                      void* dq, void* dk, void* dv, const fa_params_t* p, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  fa::Problem pb;
+  long long qrows = 0, krows = 0;
+  fa_status_t st = check(p, &pb, &qrows, &krows);
+  if (st != FA_OK || (qrows == 0 && krows == 0)) return st;
+  if (qrows > 0 && (!present(q) || !present(o) || !present(lse) || !present(dO) || !present(dq)))
+    return FA_ERR_INVALID_ARG;
+  if (krows > 0 && (!present(k) || !present(v) || !present(dk) || !present(dv))) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_ex_workspace_bytes(p);
+  if (need > 0 && (!workspace || !aligned16(workspace))) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, static_cast<float*>(workspace), pb, p->D, p->scale,
+                (int)p->dtype, g_events, g_nevents};
+  return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,
+                   int D, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  const fa_params_t p = dense(B, Hq, Hkv, S, D, scale, causal, dtype);
+  return fa_fwd_ex(q, k, v, o, lse, &p, stream);
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D) {
-  bool empty = false;
-  if (check_problem(B, Hq, Hkv, S, D, 1.0f, FA_BF16, &empty) != FA_OK || empty) return 0;
-  return round256((size_t)B * Hq * S * sizeof(float));
+  const fa_params_t p = dense(B, Hq, Hkv, S, D, 1.0f, 1, FA_BF16);
+  return fa_bwd_ex_workspace_bytes(&p);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
                    void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D, float scale, int causal,
                    fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  bool empty = false;
-  fa_status_t st = check_problem(B, Hq, Hkv, S, D, scale, dtype, &empty);
-  if (st != FA_OK || empty) return st;
-  const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv, workspace};
-  for (const void* p : ptrs)
-    if (!p || !aligned16(p)) return FA_ERR_INVALID_ARG;
-  if (workspace_bytes < fa_bwd_workspace_bytes(B, Hq, Hkv, S, D)) return FA_ERR_WORKSPACE;
-  fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, static_cast<float*>(workspace),
-                B, Hq, Hkv, S, D, scale, causal ? 1 : 0, (int)dtype, g_events, g_nevents};
-  return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const fa_params_t p = dense(B, Hq, Hkv, S, D, scale, causal, dtype);
+  return fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, &p, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

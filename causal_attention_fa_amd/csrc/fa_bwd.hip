@@ -62,11 +62,11 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 }
 
 // ------------------------------------------------------------------ dK, dV
-template <typename T, int HD, int BQ, int NW, bool CAUSAL>
+template <typename T, int HD, int BQ, int NW, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dK, T* __restrict__ dV,
-    int Hq, int Hkv, int S, float c, float scale, int nkt) {
+    Problem pb, float c, float scale, int nkt) {
   constexpr int BKV = 32 * NW;
   constexpr int NT = NW * 64;
   using Tile = RowTile<T, BQ, HD>;
@@ -86,27 +86,30 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   const int work = xcd_slice(blockIdx.x, gridDim.x);
   const int bg = work / nkt;
   const int kvt = work - bg * nkt;
-  const int b = bg / Hkv, hkv = bg - b * Hkv;
-  const int G = Hq / Hkv;
+  const int b = bg / pb.Hkv, hkv = bg - b * pb.Hkv;
+  const int G = pb.Hq / pb.Hkv;
+  const Seq sv0 = seq_of(pb, b, hkv * G, hkv);  // key side is the same for the whole group
   const int kv0 = kvt * BKV;
+  if (kv0 >= sv0.skv) return;  // a shorter sequence of a packed batch: no keys here
   const int kw0 = kv0 + 32 * w;
   const int mykv = kw0 + r;
-  const T* Kh = K + (size_t)bg * S * HD;
-  const T* Vh = V + (size_t)bg * S * HD;
+  const int off = sv0.off;
+  const T* Kh = K + sv0.kv_row0 * HD;
+  const T* Vh = V + sv0.kv_row0 * HD;
 
-  // keys past the end read key S-1: their dK, dV are never stored.  K stays
+  // keys past the end read key skv-1: their dK, dV are never stored.  K stays
   // in registers (B operand of S); V, the B operand of dP, is read from LDS
   // each tile, which keeps the kernel within 256 VGPRs (two workgroups per CU)
   vec8<T> kf[HD / 16];
   {
-    const size_t off = (size_t)min(mykv, S - 1) * HD + 8 * h;
+    const size_t o = (size_t)min(mykv, sv0.skv - 1) * HD + 8 * h;
 #pragma unroll
-    for (int t = 0; t < HD / 16; ++t) kf[t] = load8<T>(Kh + off + 16 * t);
+    for (int t = 0; t < HD / 16; ++t) kf[t] = load8<T>(Kh + o + 16 * t);
   }
   {
     TileLoader<T, BKV, HD, NT> vld;
     vld.init(tid);
-    vld.issue(Vh, kv0, S, lds_v, tid);
+    vld.issue(Vh, kv0, sv0.skv, lds_v, tid);
     vld.land(tid);  // published by the first barrier below
   }
   f32x16 dk[HD / 32], dv[HD / 32];
@@ -116,8 +119,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     dv[d] = f32x16{};
   }
 
-  const int first = CAUSAL ? (kv0 / BQ) : 0;
-  const int nqt = (S + BQ - 1) / BQ;
+  // query rows that can see one of the keys [kv0, kv0 + BKV): [qlo, qhi)
+  const int qlo = CAUSAL ? max(0, kv0 - off) : 0;
+  const int qhi = WINDOW ? min(sv0.sq, kv0 + BKV - 1 - off + pb.window + 1) : sv0.sq;
+  const int first = qlo / BQ;
+  const int nqt = qhi > qlo ? (qhi + BQ - 1) / BQ : first;
   const int per_head = nqt - first;
   const int total = G * per_head;
 
@@ -138,12 +144,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     }
   };
   auto issue = [&](int hq, int i0, int buf) {
-    const size_t qoff = ((size_t)b * Hq + hq) * S * HD;
+    const Seq sq = seq_of(pb, b, hq, hkv);
     T* base = lds + buf * kElems;
-    qld.issue(Q + qoff, i0, S, base + kOffQ, tid);
-    dold.issue(dO + qoff, i0, S, base + kOffD, tid);
+    qld.issue(Q + sq.q_row0 * HD, i0, sq.sq, base + kOffQ, tid);
+    dold.issue(dO + sq.q_row0 * HD, i0, sq.sq, base + kOffD, tid);
     if (tid < BQ) {
-      const size_t row = ((size_t)b * Hq + hq) * S + min(i0 + tid, S - 1);
+      const size_t row = sq.q_row0 + min(i0 + tid, sq.sq - 1);
       ld_l = LSE[row] * kLog2e;
       ld_d = Dd[row];
     }
@@ -172,7 +178,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     }
     const T* Qs = lds + buf * kElems + kOffQ;
     const T* dOs = lds + buf * kElems + kOffD;
-    const bool active = !CAUSAL || (i0 + BQ - 1 >= kw0);
+    // does a query of the tile see one of this wave's keys?
+    const bool active = (!CAUSAL || i0 + BQ - 1 + off >= kw0) &&
+                        (!WINDOW || i0 + off - pb.window <= kw0 + 31);
     if (active) {
       // S, dP (BQ x 32): rows = queries of the tile, columns = this wave's keys
       f32x16 s[BQ / 32], dp[BQ / 32];
@@ -187,8 +195,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
                           dp[qb]);
         }
       }
-      // queries before the key (causal) or past the end get p = 0
-      const bool edge = (CAUSAL && i0 < kw0 + 31) || (i0 + BQ > S);
+      // invisible (query, key) pairs and queries past the end get p = 0 (keys
+      // past the end only feed dK / dV columns that are never stored)
+      const bool edge = (CAUSAL && i0 + off < kw0 + 31) ||
+                        (WINDOW && i0 + BQ - 1 + off - pb.window > kw0) || (i0 + BQ > sv0.sq);
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
@@ -202,8 +212,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
             float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c, -lv[e]));
             if (edge) {
               const int q = i0 + qrow + e;
-              const bool masked = (CAUSAL && mykv > q) || q >= S;
-              p = masked ? 0.f : p;
+              const bool vis = q < sv0.sq && (!CAUSAL || mykv <= q + off) &&
+                               (!WINDOW || mykv >= q + off - pb.window);
+              p = vis ? p : 0.f;
             }
             s[qb][i] = p;
             dp[qb][i] = p * (dp[qb][i] - dvv[e]);
@@ -226,9 +237,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     __syncthreads();
   }
 
-  if (mykv < S) {
-    T* dKr = dK + (size_t)bg * S * HD + (size_t)mykv * HD;
-    T* dVr = dV + (size_t)bg * S * HD + (size_t)mykv * HD;
+  if (mykv < sv0.skv) {
+    T* dKr = dK + (sv0.kv_row0 + mykv) * HD;
+    T* dVr = dV + (sv0.kv_row0 + mykv) * HD;
 #pragma unroll
     for (int d = 0; d < HD / 32; ++d)
 #pragma unroll
@@ -242,11 +253,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
 }
 
 // ------------------------------------------------------------------ dQ
-template <typename T, int HD, int BC, int NW, bool CAUSAL>
+template <typename T, int HD, int BC, int NW, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dQ, int Hq, int Hkv, int S,
-    float c, float scale, int nqt) {
+    const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dQ, Problem pb, float c,
+    float scale, int nqt) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   using Tile = RowTile<T, BC, HD>;
@@ -260,59 +271,65 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   const int work = xcd_slice(blockIdx.x, gridDim.x);  // head-major, heaviest tile first
   const int bh = work / nqt;
   const int qt = CAUSAL ? (nqt - 1 - (work - bh * nqt)) : (work - bh * nqt);
-  const int b = bh / Hq, hq = bh - b * Hq;
-  const int hkv = hq / (Hq / Hkv);
-  const T* Qh = Q + (size_t)bh * S * HD;
-  const T* dOh = dO + (size_t)bh * S * HD;
-  const T* Kh = K + ((size_t)b * Hkv + hkv) * S * HD;
-  const T* Vh = V + ((size_t)b * Hkv + hkv) * S * HD;
+  const int b = bh / pb.Hq, hq = bh - b * pb.Hq;
+  const Seq sv = seq_of(pb, b, hq, hq / (pb.Hq / pb.Hkv));
   const int i0 = qt * BR;
+  if (i0 >= sv.sq) return;
+  const T* Kh = K + sv.kv_row0 * HD;
+  const T* Vh = V + sv.kv_row0 * HD;
   const int qw0 = i0 + 32 * w;
   const int myq = qw0 + r;
+  const int off = sv.off;
 
-  // query rows past the end read row S-1: their dQ is never stored
+  // query rows past the end read row sq-1: their dQ is never stored
   vec8<T> qf[HD / 16], df[HD / 16];
-  const int qrow = min(myq, S - 1);
+  const size_t qrow = sv.q_row0 + min(myq, sv.sq - 1);
   {
-    const size_t off = (size_t)qrow * HD + 8 * h;
+    const size_t o = qrow * HD + 8 * h;
 #pragma unroll
     for (int t = 0; t < HD / 16; ++t) {
-      qf[t] = load8<T>(Qh + off + 16 * t);
-      df[t] = load8<T>(dOh + off + 16 * t);
+      qf[t] = load8<T>(Q + o + 16 * t);
+      df[t] = load8<T>(dO + o + 16 * t);
     }
   }
-  const float lq = LSE[(size_t)bh * S + qrow] * kLog2e;
-  const float dq_d = Dd[(size_t)bh * S + qrow];
+  const float lq = LSE[qrow] * kLog2e;
+  const float dq_d = Dd[qrow];
   f32x16 acc[HD / 32];
 #pragma unroll
   for (int d = 0; d < HD / 32; ++d) acc[d] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(S, i0 + BR) : S;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  const int last = min(i0 + BR, sv.sq) - 1;
+  const int hi = CAUSAL ? min(sv.skv, last + off + 1) : sv.skv;
+  const int lo = WINDOW ? max(0, i0 + off - pb.window) : 0;
+  const int jt0 = lo / BC;
+  const int ntiles = hi > lo ? (hi + BC - 1) / BC - jt0 : 0;
 
   TileLoader<T, BC, HD, NT> kld, vld;
   kld.init(tid);
   vld.init(tid);
-  kld.issue(Kh, 0, S, lds + kOffK, tid);
-  vld.issue(Vh, 0, S, lds + kOffV, tid);
-  kld.land(tid);
-  vld.land(tid);
+  if (ntiles > 0) {
+    kld.issue(Kh, jt0 * BC, sv.skv, lds + kOffK, tid);
+    vld.issue(Vh, jt0 * BC, sv.skv, lds + kOffV, tid);
+    kld.land(tid);
+    vld.land(tid);
+  }
   __syncthreads();
 
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int j0 = jt * BC;
-    const bool more = jt + 1 < ntiles;
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = (jt0 + it) * BC;
+    const bool more = it + 1 < ntiles;
     if (more) {  // the other buffer was last read before the previous barrier
-      T* nb = lds + ((jt + 1) & 1) * kElems;
-      kld.issue(Kh, j0 + BC, S, nb + kOffK, tid);
-      vld.issue(Vh, j0 + BC, S, nb + kOffV, tid);
+      T* nb = lds + ((it + 1) & 1) * kElems;
+      kld.issue(Kh, j0 + BC, sv.skv, nb + kOffK, tid);
+      vld.issue(Vh, j0 + BC, sv.skv, nb + kOffV, tid);
     }
-    const T* Ks = lds + (jt & 1) * kElems + kOffK;
-    const T* Vs = lds + (jt & 1) * kElems + kOffV;
-    const bool active = !CAUSAL || j0 <= qw0 + 31;
+    const T* Ks = lds + (it & 1) * kElems + kOffK;
+    const T* Vs = lds + (it & 1) * kElems + kOffV;
+    const bool active = (!CAUSAL || j0 <= qw0 + 31 + off) &&
+                        (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
     if (active) {
-      const bool edge = CAUSAL ? (j0 + BC - 1 > qw0) : (j0 + BC > S);
-      const int lim = CAUSAL ? myq : S - 1;
+      const bool edge = (CAUSAL && j0 + BC - 1 > qw0 + off) ||
+                        (WINDOW && j0 < qw0 + 31 + off - pb.window) || (j0 + BC > sv.skv);
       // one 32-key block at a time: its S^T, dP^T and dS^T are dead before the
       // next block's are formed, which halves the accumulator registers
 #pragma unroll
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
           float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lq));
           if (edge) {
             const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            p = kv > lim ? 0.f : p;
+            p = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? p : 0.f;
           }
           dp[i] = p * (dp[i] - dq_d);
         }
@@ -350,8 +367,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     __syncthreads();
   }
 
-  if (myq < S) {
-    T* dQr = dQ + (size_t)bh * S * HD + (size_t)myq * HD;
+  if (myq < sv.sq) {
+    T* dQr = dQ + (sv.q_row0 + myq) * HD;
 #pragma unroll
     for (int d = 0; d < HD / 32; ++d)
 #pragma unroll
@@ -362,10 +379,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
 }
 
 // ------------------------------------------------------------------ launch
-template <typename T, int HD, bool CAUSAL>
+template <typename T, int HD, bool CAUSAL, bool WINDOW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  const long long rows = (long long)a.B * a.Hq * a.S;
-  {
+  const Problem& pb = a.pb;
+  const long long rows = pb.cu_q != nullptr ? (long long)pb.Hq * pb.Tq : (long long)pb.B * pb.Hq * pb.Sq;
+  if (rows > 0) {
     constexpr int kRowsPerBlock = 256 / (HD / Elem<T>::kEpv);
     dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
     mark(a.ev, a.nev, 0, st);
@@ -377,32 +395,40 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   {
     constexpr int NW = 4, BQ = (HD == 128 || sizeof(T) == 4) ? 32 : 64;
-    const int nkt = (a.S + 32 * NW - 1) / (32 * NW);
-    dim3 grid(nkt * a.B * a.Hkv);
+    const int nkt = (pb.Skv + 32 * NW - 1) / (32 * NW);
+    dim3 grid(nkt * pb.B * pb.Hkv);
     mark(a.ev, a.nev, 1, st);
-    hipLaunchKernelGGL((dkdv_kernel<T, HD, BQ, NW, CAUSAL>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
-                       (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dk,
-                       (T*)a.dv, a.Hq, a.Hkv, a.S, c, a.scale, nkt);
+    if (grid.x > 0)
+      hipLaunchKernelGGL((dkdv_kernel<T, HD, BQ, NW, CAUSAL, WINDOW>), grid, dim3(NW * 64), 0, st, (const T*)a.q, (const T*)a.k,
+                         (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dk, (T*)a.dv, pb, c,
+                         a.scale, nkt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     constexpr int NW = 4, BC = 64;
-    const int nqt = (a.S + 32 * NW - 1) / (32 * NW);
-    dim3 grid(nqt * a.B * a.Hq);
+    const int nqt = (pb.Sq + 32 * NW - 1) / (32 * NW);
+    dim3 grid(nqt * pb.B * pb.Hq);
     mark(a.ev, a.nev, 2, st);
-    hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
-                       (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dq,
-                       a.Hq, a.Hkv, a.S, c, a.scale, nqt);
+    if (grid.x > 0)
+      hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL, WINDOW>), grid, dim3(NW * 64), 0, st, (const T*)a.q, (const T*)a.k,
+                         (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dq, pb, c, a.scale,
+                         nqt);
     mark(a.ev, a.nev, 3, st);
     return hipGetLastError();
   }
 }
 
+template <typename T, int HD>
+static hipError_t launch_bwd_m(const BwdArgs& a, hipStream_t st) {
+  if (a.pb.window >= 0)
+    return a.pb.causal ? launch_bwd_t<T, HD, true, true>(a, st) : launch_bwd_t<T, HD, false, true>(a, st);
+  return a.pb.causal ? launch_bwd_t<T, HD, true, false>(a, st) : launch_bwd_t<T, HD, false, false>(a, st);
+}
+
 template <typename T>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
-  if (a.D == 64) return a.causal ? launch_bwd_t<T, 64, true>(a, st) : launch_bwd_t<T, 64, false>(a, st);
-  return a.causal ? launch_bwd_t<T, 128, true>(a, st) : launch_bwd_t<T, 128, false>(a, st);
+  return a.D == 64 ? launch_bwd_m<T, 64>(a, st) : launch_bwd_m<T, 128>(a, st);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {

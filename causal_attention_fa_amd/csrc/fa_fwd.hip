@@ -5,7 +5,8 @@
 // "FA2 算法" (Q tile outer, loaded once; KV tiles inner; running max / sum with
 // rescale by exp(m - m_new)); section "Causal Mask" (tiles wholly after the
 // diagonal are skipped, the rest masked per element); section "GQA 支持"
-// (KV head = query head / group size, indexed in the kernel).  L = m + log l is
+// (KV head = query head / group size, indexed in the kernel), where a longer
+// key sequence is aligned bottom-right (kv_offset = kv_len - q_len).  L = m + log l is
 // the forward's saved state ("Phase T14: 融合 Flash-Attention Kernel — Design
 // Document", section "什么是 flash-attention" and decision ②).
 //
@@ -25,8 +26,10 @@
 //   * the row sum l is one more MFMA per step (all-ones A operand), so it sums
 //     exactly the rounded P that multiplies V;
 //   * causal: workgroups are launched heaviest (last query tiles) first, a wave
-//     skips KV tiles that lie wholly after its rows, and the element mask is
-//     applied on diagonal tiles only;
+//     skips KV tiles that lie wholly after its rows (or, with a window, wholly
+//     before them), and the element mask is applied on edge tiles only;
+//   * packed variable-length batches: a workgroup past its sequence's end
+//     returns at once; every sequence has its own key offset;
 //   * each XCD takes a contiguous run of heads, so the query heads of a KV
 //     group stream that group's K/V through one L2.
 #include "fa_common.hpp"
@@ -42,10 +45,10 @@ namespace fa {
 // long-context workload), while 2^8 with an unrounded l does not.
 constexpr float kRescaleLog2 = 4.f;
 
-template <typename T, int HD, int BC, int NW, bool CAUSAL>
+template <typename T, int HD, int BC, int NW, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
-    float* __restrict__ LSE, int Hq, int Hkv, int S, float c, int nqt) {
+    float* __restrict__ LSE, Problem pb, float c, int nqt) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   using Tile = RowTile<T, BC, HD>;
@@ -59,18 +62,20 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   const int work = xcd_slice(blockIdx.x, gridDim.x);
   const int bh = work / nqt;
   const int qt = CAUSAL ? (nqt - 1 - (work - bh * nqt)) : (work - bh * nqt);
-  const int b = bh / Hq, hq = bh - b * Hq;
-  const int hkv = hq / (Hq / Hkv);
-  const T* Qh = Q + (size_t)bh * S * HD;
-  const T* Kh = K + ((size_t)b * Hkv + hkv) * S * HD;
-  const T* Vh = V + ((size_t)b * Hkv + hkv) * S * HD;
+  const int b = bh / pb.Hq, hq = bh - b * pb.Hq;
+  const Seq sv = seq_of(pb, b, hq, hq / (pb.Hq / pb.Hkv));
   const int i0 = qt * BR;
+  if (i0 >= sv.sq) return;  // a shorter sequence of a packed batch: no rows here
+  const T* Qh = Q + sv.q_row0 * HD;
+  const T* Kh = K + sv.kv_row0 * HD;
+  const T* Vh = V + sv.kv_row0 * HD;
   const int qw0 = i0 + 32 * w;
   const int myq = qw0 + r;
+  const int off = sv.off;
 
-  // rows past the end read row S-1: their results are never stored
+  // rows past the end read row sq-1: their results are never stored
   vec8<T> qf[HD / 16];
-  const T* qrow = Qh + (size_t)min(myq, S - 1) * HD + 8 * h;
+  const T* qrow = Qh + (size_t)min(myq, sv.sq - 1) * HD + 8 * h;
 #pragma unroll
   for (int t = 0; t < HD / 16; ++t) qf[t] = load8<T>(qrow + 16 * t);
 
@@ -86,29 +91,37 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   for (int j = 0; j < 8; ++j) ones[j] = to_elem<T>(1.f);
   float m = -INFINITY;
 
-  const int kv_end = CAUSAL ? min(S, i0 + BR) : S;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  // keys the workgroup's rows can see: [lo, hi)
+  const int last = min(i0 + BR, sv.sq) - 1;
+  const int hi = CAUSAL ? min(sv.skv, last + off + 1) : sv.skv;
+  const int lo = WINDOW ? max(0, i0 + off - pb.window) : 0;
+  const int jt0 = lo / BC;
+  const int ntiles = hi > lo ? (hi + BC - 1) / BC - jt0 : 0;
 
   TileLoader<T, BC, HD, NT> kld, vld;
   kld.init(tid);
   vld.init(tid);
-  kld.issue(Kh, 0, S, lds, tid);
-  vld.issue(Vh, 0, S, lds + Tile::kElems, tid);
-  kld.land(tid);
-  vld.land(tid);
+  if (ntiles > 0) {
+    kld.issue(Kh, jt0 * BC, sv.skv, lds, tid);
+    vld.issue(Vh, jt0 * BC, sv.skv, lds + Tile::kElems, tid);
+    kld.land(tid);
+    vld.land(tid);
+  }
   __syncthreads();
 
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int j0 = jt * BC;
-    const bool more = jt + 1 < ntiles;
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = (jt0 + it) * BC;
+    const bool more = it + 1 < ntiles;
     if (more) {  // the other buffer was last read before the previous barrier
-      T* nb = lds + ((jt + 1) & 1) * kBuf;
-      kld.issue(Kh, j0 + BC, S, nb, tid);
-      vld.issue(Vh, j0 + BC, S, nb + Tile::kElems, tid);
+      T* nb = lds + ((it + 1) & 1) * kBuf;
+      kld.issue(Kh, j0 + BC, sv.skv, nb, tid);
+      vld.issue(Vh, j0 + BC, sv.skv, nb + Tile::kElems, tid);
     }
-    const T* Ks = lds + (jt & 1) * kBuf;
+    const T* Ks = lds + (it & 1) * kBuf;
     const T* Vs = Ks + Tile::kElems;
-    const bool active = !CAUSAL || j0 <= qw0 + 31;
+    // does any of this wave's rows see a key of the tile?
+    const bool active = (!CAUSAL || j0 <= qw0 + 31 + off) &&
+                        (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
     if (active) {
       // S^T (BC x 32) = K_tile Q_w^T
       f32x16 s[BC / 32];
@@ -118,16 +131,16 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 #pragma unroll
         for (int t = 0; t < HD / 16; ++t) s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
       }
-      // keys after the query (causal) or past the end (last tile) get -inf
-      const bool edge = CAUSAL ? (j0 + BC - 1 > qw0) : (j0 + BC > S);
+      // invisible keys (causal / window / past the end) get -inf
+      const bool edge = (CAUSAL && j0 + BC - 1 > qw0 + off) ||
+                        (WINDOW && j0 < qw0 + 31 + off - pb.window) || (j0 + BC > sv.skv);
       if (edge) {
-        const int lim = CAUSAL ? myq : S - 1;
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            s[kb][i] = kv > lim ? -INFINITY : s[kb][i];
+            s[kb][i] = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? s[kb][i] : -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -136,11 +149,12 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
       mx = wave_xor32_max(mx) * c;
-      // Move the reference only when a row's max outgrows it by 2^8 (any lane:
+      // Move the reference only when a row's max outgrows it by 2^4 (any lane:
       // the branch is wave-uniform).  O = acc / l is exact for any reference.
       if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
         const float m_new = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        // a row that has seen no key keeps m = -inf and alpha = 1
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
         lacc *= alpha;
 #pragma unroll
         for (int d = 0; d < HD / 32; ++d) oacc[d] *= alpha;
@@ -168,35 +182,43 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   }
 
   const float l = lacc[0];
-  if (myq < S) {
-    const float inv = 1.f / l;
-    T* Or = O + (size_t)bh * S * HD + (size_t)myq * HD;
+  if (myq < sv.sq) {
+    // a row that saw no key has an empty softmax: O = 0, L = -inf
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    T* Or = O + (sv.q_row0 + myq) * HD;
 #pragma unroll
     for (int d = 0; d < HD / 32; ++d)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         store4<T>(Or + 32 * d + 8 * g + 4 * h, oacc[d][4 * g] * inv, oacc[d][4 * g + 1] * inv,
                   oacc[d][4 * g + 2] * inv, oacc[d][4 * g + 3] * inv);
-    if (LSE != nullptr && h == 0) LSE[(size_t)bh * S + myq] = (m + log2f(l)) * kLn2;
+    if (LSE != nullptr && h == 0) LSE[sv.q_row0 + myq] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
-template <typename T, int HD, bool CAUSAL>
+template <typename T, int HD, bool CAUSAL, bool WINDOW>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   constexpr int NW = 4, BC = 64, BR = 32 * NW;
-  const int nqt = (a.S + BR - 1) / BR;
-  dim3 grid(nqt * a.B * a.Hq), block(NW * 64);
+  const int nqt = (a.pb.Sq + BR - 1) / BR;
+  dim3 grid(nqt * a.pb.B * a.pb.Hq), block(NW * 64);
   mark(a.ev, a.nev, 0, st);
-  hipLaunchKernelGGL((fwd_kernel<T, HD, BC, NW, CAUSAL>), grid, block, 0, st, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (T*)a.o, a.lse, a.Hq, a.Hkv, a.S, a.scale * kLog2e, nqt);
+  if (grid.x > 0)
+    hipLaunchKernelGGL((fwd_kernel<T, HD, BC, NW, CAUSAL, WINDOW>), grid, block, 0, st, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.pb, a.scale * kLog2e, nqt);
   mark(a.ev, a.nev, 1, st);
   return hipGetLastError();
 }
 
+template <typename T, int HD>
+static hipError_t launch_fwd_m(const FwdArgs& a, hipStream_t st) {
+  if (a.pb.window >= 0)
+    return a.pb.causal ? launch_fwd_t<T, HD, true, true>(a, st) : launch_fwd_t<T, HD, false, true>(a, st);
+  return a.pb.causal ? launch_fwd_t<T, HD, true, false>(a, st) : launch_fwd_t<T, HD, false, false>(a, st);
+}
+
 template <typename T>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t st) {
-  if (a.D == 64) return a.causal ? launch_fwd_t<T, 64, true>(a, st) : launch_fwd_t<T, 64, false>(a, st);
-  return a.causal ? launch_fwd_t<T, 128, true>(a, st) : launch_fwd_t<T, 128, false>(a, st);
+  return a.D == 64 ? launch_fwd_m<T, 64>(a, st) : launch_fwd_m<T, 128>(a, st);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {

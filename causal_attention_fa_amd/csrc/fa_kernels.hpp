@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "fa_problem.hpp"
+
 namespace fa {
 
 struct FwdArgs {
@@ -12,9 +14,9 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int B, Hq, Hkv, S, D;
+  Problem pb;
+  int D;
   float scale;
-  int causal;
   int dtype;  // 0 fp32, 1 fp16, 2 bf16 (fa_dtype_t)
   hipEvent_t* ev;  // optional timing events (fa_profile_events), nev of them
   int nev;
@@ -35,10 +37,10 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* rowdot;  // workspace: D[i] = sum_d dO[i,d] * O[i,d], [B*Hq*S] fp32
-  int B, Hq, Hkv, S, D;
+  float* rowdot;  // workspace: D[i] = sum_d dO[i,d] * O[i,d], one fp32 per query row
+  Problem pb;
+  int D;
   float scale;
-  int causal;
   int dtype;
   hipEvent_t* ev;
   int nev;

@@ -1,0 +1,60 @@
+// fa_problem.hpp -- the attention problem as the kernels see it: dense batches
+// ([B][H][S][D]) or packed variable-length batches ([H][T][D] with cumulative
+// sequence offsets), queries and keys of different lengths, an optional left
+// window.  Shared by the host launchers and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct Problem {
+  int B, Hq, Hkv;
+  int Sq, Skv;        // dense: the lengths; packed: upper bounds of the per-sequence lengths
+  int causal;         // key j visible to query i iff j <= i + (skv - sq)
+  int window;         // < 0: none; else also j >= i + (skv - sq) - window
+  const int* cu_q;    // packed: B + 1 cumulative query offsets (device); nullptr: dense
+  const int* cu_k;
+  int Tq, Tk;         // packed: rows per head slab of q/o/dq and of k/v/dk/dv
+};
+
+// One (batch, query head, KV head) sequence.  Rows of its queries are
+// q_row0 .. q_row0 + sq - 1 of the [rows][D] view of q (and of o, dq, lse, the
+// row-dot workspace); its keys are kv_row0 .. kv_row0 + skv - 1 of k (v, dk, dv).
+struct Seq {
+  size_t q_row0, kv_row0;
+  int sq, skv, off;
+};
+
+// Packed offsets are clamped into [0, T] and lengths to the stated maxima, so
+// malformed offsets can make results wrong but never move an access out of
+// the buffers the caller described.
+__device__ inline Seq seq_of(const Problem& p, int b, int hq, int hkv) {
+  Seq s;
+  if (p.cu_q != nullptr) {
+    const int q0 = min(max(p.cu_q[b], 0), p.Tq);
+    const int q1 = min(max(p.cu_q[b + 1], q0), p.Tq);
+    const int k0 = min(max(p.cu_k[b], 0), p.Tk);
+    const int k1 = min(max(p.cu_k[b + 1], k0), p.Tk);
+    s.sq = min(q1 - q0, p.Sq);
+    s.skv = min(k1 - k0, p.Skv);
+    s.q_row0 = (size_t)hq * p.Tq + q0;
+    s.kv_row0 = (size_t)hkv * p.Tk + k0;
+  } else {
+    s.sq = p.Sq;
+    s.skv = p.Skv;
+    s.q_row0 = ((size_t)b * p.Hq + hq) * p.Sq;
+    s.kv_row0 = ((size_t)b * p.Hkv + hkv) * p.Skv;
+  }
+  s.off = s.skv - s.sq;
+  return s;
+}
+
+// Visibility of key j to query i (both relative to their sequence); the mask
+// kinds are compile-time so the common causal-only path carries no window.
+template <bool CAUSAL, bool WINDOW>
+__device__ inline bool key_visible(const Problem& p, const Seq& s, int i, int j) {
+  return j < s.skv && (!CAUSAL || j <= i + s.off) && (!WINDOW || j >= i + s.off - p.window);
+}
+
+}  // namespace fa

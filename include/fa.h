@@ -38,10 +38,11 @@
  * Errors: arguments are checked on the host before anything is enqueued; on
  * any error nothing is launched and no output is touched.
  *   FA_ERR_INVALID_ARG   null required pointer; B, Hq, Hkv, S or D < 0;
- *                        Hkv == 0 while B*Hq*S > 0; Hq % Hkv != 0;
- *                        scale not finite; a pointer not 16-byte aligned;
- *                        dtype not one of fa_dtype_t.
- *   FA_ERR_UNSUPPORTED   D not 64 or 128; scale <= 0.
+ *                        B, Hq or Hkv == 0 while there are query or key
+ *                        rows; Hq % Hkv != 0; scale not finite; a pointer
+ *                        not 16-byte aligned; dtype not one of fa_dtype_t.
+ *   FA_ERR_UNSUPPORTED   D not 64 or 128; scale <= 0; a sequence length
+ *                        above 2^29 (or a grid beyond INT_MAX workgroups).
  *   FA_ERR_WORKSPACE     workspace smaller than fa_bwd_workspace_bytes().
  *   FA_ERR_HIP           a HIP launch reported an error (hipGetLastError).
  * A problem with B * Hq * S == 0 is a no-op that returns FA_OK once the
@@ -110,6 +111,66 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
 
 /* Static, human-readable name of a status code ("FA_OK", ...); never NULL. */
 const char* fa_status_string(fa_status_t s);
+
+/*
+ * Extended problems: queries and keys of different lengths, a sliding window,
+ * and packed variable-length batches.
+ *
+ *   Visibility of key j to query i of one sequence, offset = Skv_b - Sq_b:
+ *     causal        j <= i + offset          (bottom-right alignment: "Phase 14",
+ *                                             section Causal Mask, kv_offset)
+ *     window >= 0   j >= i + offset - window (a left window of window + 1 keys
+ *                                             when causal; window >= Skv hides
+ *                                             nothing and runs as no window)
+ *   A query that sees no key has an empty softmax: its O row is 0, its L is
+ *   -inf, and it contributes no gradient.
+ *
+ *   Dense batches (cu_seqlens_q == cu_seqlens_k == NULL):
+ *     q, o, dO, dq [B][Hq][Sq][D]; k, v, dk, dv [B][Hkv][Skv][D]; lse [B][Hq][Sq]
+ *   Packed variable-length batches (both non-NULL, device int32 arrays of B + 1
+ *   non-decreasing offsets starting at 0): sequence b owns query rows
+ *   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ *   cu_seqlens_k[b+1]-1, and
+ *     q, o, dO, dq [Hq][total_q][D]; k, v, dk, dv [Hkv][total_k][D];
+ *     lse [Hq][total_q]
+ *   where total_q = cu_seqlens_q[B] and total_k = cu_seqlens_k[B] are also
+ *   passed by value, and Sq / Skv are upper bounds of the per-sequence lengths
+ *   (they size the launch).  The kernels clamp offsets into [0, total] and
+ *   lengths to the bounds, so malformed offsets give wrong results, never
+ *   accesses outside the described buffers.
+ */
+typedef struct {
+  int B, Hq, Hkv;
+  int Sq, Skv;                 /* lengths (dense) or length bounds (packed) */
+  int D;                       /* 64 or 128 */
+  float scale;                 /* finite, > 0 */
+  int causal;                  /* 0 or 1 */
+  int window;                  /* < 0: no window */
+  const int* cu_seqlens_q;     /* device, B + 1 entries, or NULL */
+  const int* cu_seqlens_k;     /* device, B + 1 entries, or NULL */
+  int total_q, total_k;        /* packed only: cu_seqlens_q[B], cu_seqlens_k[B] */
+  fa_dtype_t dtype;
+} fa_params_t;
+
+/* Forward of an extended problem.  Same outputs and errors as fa_fwd; also
+ * FA_ERR_INVALID_ARG for a NULL params, only one of the cu_seqlens pointers
+ * given, a cu_seqlens pointer not 4-byte aligned, or negative totals.
+ * A problem with no query row is a no-op; with no key row, k and v may be
+ * NULL and every O row is 0, every L -inf. */
+fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const fa_params_t* params, hipStream_t stream);
+
+/* Workspace of fa_bwd_ex (fp32 row dot products, one per query row; a multiple of
+ * 256 bytes), or 0 when none is needed or the params are rejected. */
+size_t fa_bwd_ex_workspace_bytes(const fa_params_t* params);
+
+/* Backward of an extended problem (as fa_bwd).  dk and dv of keys no query can
+ * see are written as 0; the call is a no-op only when there are neither query
+ * nor key rows.  Buffers of an empty side (q, o, lse, dO, dq without query
+ * rows; k, v, dk, dv without key rows) may be NULL. */
+fa_status_t fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dO, void* dq, void* dk, void* dv, const fa_params_t* params,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Instrumentation for benchmarks (not part of the computation).  After

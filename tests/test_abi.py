@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_profile_events", "fa_status_string"]
+    assert names == ["fa_bwd", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes", "fa_bwd_workspace_bytes", "fa_fwd",
+                     "fa_fwd_ex", "fa_profile_events", "fa_status_string"]
     L = fa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -122,3 +123,110 @@ def test_python_wrappers_need_device_tensors():
     q = torch.zeros(1, 2, 8, 64)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+# ------------------------------------------------------------------ extended problems
+
+def test_params_struct_layout():
+    import ctypes
+    P = fa.fa_params_t
+    # int B,Hq,Hkv,Sq,Skv,D; float scale; int causal, window; two pointers; int total_q, total_k; enum dtype
+    assert P.scale.offset == 24 and P.window.offset == 32
+    assert P.cu_seqlens_q.offset == 40 and P.cu_seqlens_k.offset == 48
+    assert P.total_q.offset == 56 and P.dtype.offset == 64 and ctypes.sizeof(P) == 72
+
+
+def ex_params(**kw):
+    base = dict(B=1, Hq=4, Hkv=2, Sq=16, Skv=24, D=64, scale=0.125, causal=True, window=None,
+                dtype=fa.FA_BF16)
+    base.update(kw)
+    return fa.params(**base)
+
+
+def fwd_ex(p=None, **kw):
+    args = dict(q=A, k=A, v=A, o=A, lse=A, stream=None)
+    args.update(kw)
+    return fa.fa_fwd_ex(args["q"], args["k"], args["v"], args["o"], args["lse"],
+                        ex_params() if p is None else p, args["stream"])
+
+
+def bwd_ex(p=None, **kw):
+    p = ex_params() if p is None else p
+    args = dict(q=A, k=A, v=A, o=A, lse=A, dO=A, dq=A, dk=A, dv=A, workspace=A,
+                workspace_bytes=fa.fa_bwd_ex_workspace_bytes(p), stream=None)
+    args.update(kw)
+    return fa.fa_bwd_ex(args["q"], args["k"], args["v"], args["o"], args["lse"], args["dO"], args["dq"],
+                        args["dk"], args["dv"], p, args["workspace"], args["workspace_bytes"], args["stream"])
+
+
+def test_ex_null_params():
+    assert fa.lib().fa_fwd_ex(A, A, A, A, A, None, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.lib().fa_bwd_ex(A, A, A, A, A, A, A, A, A, None, A, 1 << 20, None) == fa.FA_ERR_INVALID_ARG
+    assert fa.lib().fa_bwd_ex_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("call", [fwd_ex, bwd_ex])
+@pytest.mark.parametrize("pk,expect", [
+    ({"Sq": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"Skv": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"Hq": 3}, fa.FA_ERR_INVALID_ARG),
+    ({"Hq": 0}, fa.FA_ERR_INVALID_ARG),          # key rows but no query head
+    ({"B": 0}, fa.FA_OK),
+    ({"Sq": 0, "Skv": 0}, fa.FA_OK),
+    ({"D": 96}, fa.FA_ERR_UNSUPPORTED),
+    ({"scale": 0.0}, fa.FA_ERR_UNSUPPORTED),
+    ({"scale": math.nan}, fa.FA_ERR_INVALID_ARG),
+    ({"dtype": 5}, fa.FA_ERR_INVALID_ARG),
+    ({"cu_seqlens_q": A}, fa.FA_ERR_INVALID_ARG),                       # only one offset array
+    ({"cu_seqlens_k": A}, fa.FA_ERR_INVALID_ARG),
+    ({"cu_seqlens_q": A + 2, "cu_seqlens_k": A, "total_q": 4, "total_k": 4}, fa.FA_ERR_INVALID_ARG),
+    ({"cu_seqlens_q": A, "cu_seqlens_k": A, "total_q": -1, "total_k": 4}, fa.FA_ERR_INVALID_ARG),
+    ({"cu_seqlens_q": A, "cu_seqlens_k": A, "total_q": 0, "total_k": 0}, fa.FA_OK),
+    ({"Sq": (1 << 29) + 1}, fa.FA_ERR_UNSUPPORTED),
+    ({"Skv": (1 << 29) + 1}, fa.FA_ERR_UNSUPPORTED),
+    ({"B": 1 << 20, "Hq": 1 << 10, "Hkv": 1 << 10, "Sq": 1 << 10, "Skv": 16}, fa.FA_ERR_UNSUPPORTED),
+])
+def test_ex_argument_checks(call, pk, expect):
+    assert call(ex_params(**pk)) == expect
+
+
+def test_ex_forward_empty_sides():
+    # no query rows: nothing to compute, no pointer is needed
+    assert fwd_ex(ex_params(Sq=0), q=None, k=None, v=None, o=None, lse=None) == fa.FA_OK
+    # query rows need q and o
+    assert fwd_ex(q=None) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(o=A + 4) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(lse=A + 4) == fa.FA_ERR_INVALID_ARG
+    # key rows need k and v
+    assert fwd_ex(k=None) == fa.FA_ERR_INVALID_ARG
+    assert fwd_ex(v=A + 8) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [{"lse": None}, {"dO": None}, {"dq": A + 8}, {"dk": None}, {"dv": A + 4},
+                                {"q": None}, {"k": None}])
+def test_ex_backward_pointer_checks(kw):
+    assert bwd_ex(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_ex_backward_workspace():
+    p = ex_params()
+    n = fa.fa_bwd_ex_workspace_bytes(p)
+    assert n == 256                                      # 4 heads x 16 rows x 4 bytes, rounded up
+    assert bwd_ex(p, workspace_bytes=n - 1) == fa.FA_ERR_WORKSPACE
+    assert bwd_ex(p, workspace=None) == fa.FA_ERR_INVALID_ARG
+    big = ex_params(Hq=32, Hkv=8, Sq=16384, Skv=16384, D=128)
+    assert fa.fa_bwd_ex_workspace_bytes(big) == 32 * 16384 * 4
+    packed = ex_params(cu_seqlens_q=A, cu_seqlens_k=A, total_q=1000, total_k=3000, B=5)
+    assert fa.fa_bwd_ex_workspace_bytes(packed) == 16128   # heads x total query rows x 4 bytes, to 256
+    assert fa.fa_bwd_ex_workspace_bytes(ex_params(Hq=3)) == 0
+
+
+def test_ex_backward_without_queries_needs_no_query_buffers():
+    # keys but no queries: dk and dv are still written (zeros), so only the key-side buffers are needed,
+    # but that is a launch: the empty-problem form (no rows at all) is the only pure host case here
+    p = ex_params(Sq=0, Skv=0)
+    assert bwd_ex(p, q=None, k=None, v=None, o=None, lse=None, dO=None, dq=None, dk=None, dv=None,
+                  workspace=None) == fa.FA_OK
+    p = ex_params(Sq=0)
+    assert fa.fa_bwd_ex_workspace_bytes(p) == 0
+    assert bwd_ex(p, dk=None) == fa.FA_ERR_INVALID_ARG     # key rows need dk, checked before any launch

@@ -1,0 +1,214 @@
+"""GPU parity of the extended problems against the fp64 CPU oracle.
+
+Covers queries and keys of different lengths (causal diagonal aligned
+bottom-right), sliding windows, and packed variable-length batches, through
+``fa_fwd_ex`` / ``fa_bwd_ex`` (and, for equal lengths without a window, the
+plain entry points for comparison).  Tolerances are those of ``test_parity``.
+
+Rows that see no key (a causal problem with fewer keys than queries, or a
+sequence with no keys) have O = 0 and L = -inf on both sides; the -inf
+positions must agree exactly and the finite L values meet the usual bound.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import causal_attention_fa_amd as fa
+import oracle
+from workloads import make_inputs, make_varlen_inputs
+
+from test_parity import TOL, check_grads, check_o, dev, host, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def check_lse(got, ref, dtype, what=""):
+    gi, ri = np.isneginf(got), np.isneginf(ref)
+    assert np.array_equal(gi, ri), f"{what} L = -inf at different rows ({int(gi.sum())} vs {int(ri.sum())})"
+    if (~ri).any():
+        e = float(np.abs(got[~ri] - ref[~ri]).max())
+        assert e <= TOL[dtype]["lse"], f"{what} L max-abs {e:.3e}"
+    assert not np.isnan(got).any()
+
+
+def run_dense(inp, dtype, scale, causal, window):
+    q, k, v, do = (dev(inp[n], dtype) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, scale=scale, causal=causal, window=window)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, scale=scale, causal=causal, window=window)
+    torch.cuda.synchronize()
+    return host(o), host(lse), (host(dq), host(dk), host(dv))
+
+
+def compare(got, ref, dtype, what):
+    o, lse, grads = got
+    check_o(o, ref["o"], dtype, what)
+    check_lse(lse, ref["lse"], dtype, what)
+    check_grads(grads, (ref["dq"], ref["dk"], ref["dv"]), dtype, what)
+
+
+# ------------------------------------------------------------------ Sq != Skv
+
+CROSS = []
+for Sq, Skv in ((1, 257), (33, 200), (200, 33), (64, 81), (129, 65), (65, 1)):
+    for D in (64, 128):
+        for dtype in ("f32", "bf16"):
+            for causal in (True, False):
+                CROSS.append((Sq, Skv, D, dtype, causal))
+
+
+@pytest.mark.parametrize("Sq,Skv,D,dtype,causal", CROSS)
+def test_cross_length(Sq, Skv, D, dtype, causal):
+    G = (1, 2, 4)[(Sq + Skv + D) % 3]
+    B, Hkv = 2, 2
+    scale = 1.0 / math.sqrt(D)
+    inp = make_inputs(B, Hkv * G, Hkv, Sq, D, dtype, seed=2000 + Sq + 3 * Skv, q_std=1.5, Skv=Skv)
+    what = f"Sq={Sq} Skv={Skv} D={D} {dtype} causal={causal} G={G}"
+    say("case", what)
+    ref = oracle.sdpa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal)
+    compare(run_dense(inp, dtype, scale, causal, None), ref, dtype, what)
+
+
+# ------------------------------------------------------------------ sliding window
+
+WINDOWS = []
+for Sq, Skv, win in ((300, 300, 0), (300, 300, 1), (300, 300, 31), (300, 300, 64), (300, 300, 100),
+                     (257, 513, 40), (513, 257, 200), (130, 130, 1000)):
+    for causal in (True, False):
+        for dtype, D in (("bf16", 128), ("f32", 64), ("f16", 64)):
+            WINDOWS.append((Sq, Skv, win, causal, dtype, D))
+
+
+@pytest.mark.parametrize("Sq,Skv,window,causal,dtype,D", WINDOWS)
+def test_window(Sq, Skv, window, causal, dtype, D):
+    G = 2 if D == 128 else 1
+    B, Hkv = 1, 2
+    scale = 1.0 / math.sqrt(D)
+    inp = make_inputs(B, Hkv * G, Hkv, Sq, D, dtype, seed=3000 + window + Sq, q_std=1.5, Skv=Skv)
+    what = f"Sq={Sq} Skv={Skv} window={window} causal={causal} {dtype} D={D}"
+    say("case", what)
+    ref = oracle.sdpa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, window=window)
+    compare(run_dense(inp, dtype, scale, causal, window), ref, dtype, what)
+
+
+def test_no_keys_dense():
+    """Skv = 0: every row's softmax is empty: O = 0, L = -inf, dQ = 0."""
+    inp = make_inputs(1, 2, 1, 37, 64, "bf16", seed=7, Skv=0)
+    say("case Skv=0")
+    o, lse, (dq, dk, dv) = run_dense(inp, "bf16", 0.125, True, None)
+    assert not o.any() and np.isneginf(lse).all() and not dq.any()
+    assert dk.shape == (1, 1, 0, 64) and dv.shape == (1, 1, 0, 64)
+
+
+def test_no_queries_dense():
+    """Sq = 0 with keys: no query sees a key, so dK = dV = 0 (written, not left stale)."""
+    Sq, Skv, D = 0, 100, 128
+    q = torch.empty(1, 4, Sq, D, device="cuda:0", dtype=torch.bfloat16)
+    k = torch.randn(1, 2, Skv, D, device="cuda:0").to(torch.bfloat16)
+    v = torch.randn_like(k)
+    say("case Sq=0")
+    o, lse = fa.forward(q, k, v, window=5)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, torch.empty_like(q), window=5)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape and dq.shape == q.shape
+    assert not dk.float().abs().sum().item() and not dv.float().abs().sum().item()
+
+
+# ------------------------------------------------------------------ packed variable-length batches
+
+VARLEN = [
+    # (query lengths, key lengths, causal, window, dtype, D)
+    ((0, 1, 63, 64, 129, 300, 5), (0, 1, 63, 64, 129, 300, 5), True, None, "bf16", 128),
+    ((0, 1, 63, 64, 129, 300, 5), (0, 1, 63, 64, 129, 300, 5), False, None, "f32", 64),
+    ((7, 1, 100, 64, 200, 31, 5, 0), (17, 1, 40, 64, 65, 300, 0, 23), True, None, "bf16", 64),
+    ((7, 1, 100, 64, 200, 31, 5, 0), (17, 1, 40, 64, 65, 300, 0, 23), False, None, "f16", 128),
+    ((129, 300, 1, 64), (129, 300, 1, 64), True, 32, "bf16", 128),
+    ((50, 300, 1, 64), (129, 200, 9, 64), True, 20, "f32", 128),
+    ((50, 300, 1, 64), (129, 200, 9, 64), False, 70, "bf16", 64),
+]
+
+
+def run_varlen(inp, dtype, scale, causal, window, Hq):
+    q, k, v, do = (dev(inp[n], dtype) for n in ("q", "k", "v", "do"))
+    cu_q = torch.from_numpy(inp["cu_q"]).to("cuda:0")
+    cu_k = torch.from_numpy(inp["cu_k"]).to("cuda:0")
+    mq = int(np.diff(inp["cu_q"]).max())
+    mk = int(np.diff(inp["cu_k"]).max())
+    o, lse = fa.forward_varlen(q, k, v, cu_q, cu_k, mq, mk, scale=scale, causal=causal, window=window)
+    dq, dk, dv = fa.backward_varlen(q, k, v, o, lse, do, cu_q, cu_k, mq, mk, scale=scale, causal=causal,
+                                    window=window)
+    torch.cuda.synchronize()
+    return host(o), host(lse), (host(dq), host(dk), host(dv))
+
+
+@pytest.mark.parametrize("case", range(len(VARLEN)))
+def test_varlen(case):
+    sq, sk, causal, window, dtype, D = VARLEN[case]
+    Hq, Hkv = 4, 2
+    scale = 1.0 / math.sqrt(D)
+    inp = make_varlen_inputs(sq, sk, Hq, Hkv, D, dtype, seed=4000 + case, q_std=1.5)
+    what = f"varlen q={sq} k={sk} causal={causal} window={window} {dtype} D={D}"
+    say("case", what)
+    ref = oracle.sdpa_backward_varlen(inp["q"], inp["k"], inp["v"], inp["do"], inp["cu_q"], inp["cu_k"],
+                                      scale, causal, window)
+    compare(run_varlen(inp, dtype, scale, causal, window, Hq), ref, dtype, what)
+
+
+def test_varlen_matches_dense_calls_bitwise():
+    """At full size (16401 packed tokens, 32 query / 8 KV heads, D = 128, bf16): every
+    sequence of the packed call equals a dense call on that sequence alone, bit for
+    bit (same kernels, same per-tile arithmetic), and sampled rows meet the oracle."""
+    lens = (8192, 4096, 2048, 1024, 512, 256, 128, 64, 64, 17)
+    Hq, Hkv, D, dtype = 32, 8, 128, "bf16"
+    scale = 1.0 / math.sqrt(D)
+    inp = make_varlen_inputs(lens, lens, Hq, Hkv, D, dtype, seed=4100, q_std=3.0)
+    say("case varlen full size", lens)
+    o, lse, (dq, dk, dv) = run_varlen(inp, dtype, scale, True, None, Hq)
+    cu = inp["cu_q"]
+    for b in (0, 4, 9):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        sub = {n: np.ascontiguousarray(inp[n][None, :, r0:r1]) for n in ("q", "k", "v", "do")}
+        do_, dl, (dq_, dk_, dv_) = run_dense(sub, dtype, scale, True, None)
+        for name, a, ref in (("o", o[:, r0:r1], do_[0]), ("lse", lse[:, r0:r1], dl[0]),
+                             ("dq", dq[:, r0:r1], dq_[0]), ("dk", dk[:, r0:r1], dk_[0]),
+                             ("dv", dv[:, r0:r1], dv_[0])):
+            assert np.array_equal(a, ref), f"sequence {b} {name} differs from the dense call"
+    rng = np.random.default_rng(5)
+    dq_got, dq_ref = [], []
+    for b in (0, 2, 9):
+        r0, n = int(cu[b]), lens[b]
+        rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 6)]))
+        for h in (0, 13, 31):
+            sub = {x: inp[x][None, :, r0:r0 + n] for x in ("q", "k", "v", "do")}
+            O, L = oracle.sdpa_forward_rows(sub["q"], sub["k"], sub["v"], scale, True, 0, h, rows)
+            check_o(o[h, r0 + rows], O, dtype, f"seq {b} head {h}")
+            check_lse(lse[h, r0 + rows], L, dtype, f"seq {b} head {h}")
+            dq_ref.append(oracle.sdpa_dq_rows(sub["q"], sub["k"], sub["v"], sub["do"], scale, True, 0, h, rows))
+            dq_got.append(dq[h, r0 + rows])
+    e = rel_l2(np.concatenate(dq_got), np.concatenate(dq_ref))
+    assert e <= TOL[dtype]["grad"], f"sampled dQ rows rel-L2 {e:.3e}"
+
+
+def test_equal_lengths_ex_matches_plain_bitwise():
+    """fa_fwd_ex / fa_bwd_ex with Sq = Skv and no window is the plain problem."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 333, 128
+    inp = make_inputs(B, Hq, Hkv, S, D, "bf16", seed=11)
+    q, k, v, do = (dev(inp[n], "bf16") for n in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(D)
+    say("case ex == plain")
+    o1, l1 = fa.forward(q, k, v, scale=scale)
+    g1 = fa.backward(q, k, v, o1, l1, do, scale=scale)
+    s = torch.cuda.current_stream().cuda_stream
+    p = fa.params(B, Hq, Hkv, S, S, D, scale, True, None, fa.FA_BF16)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    assert fa.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(), l2.data_ptr(), p, s) == fa.FA_OK
+    g2 = [torch.empty_like(t) for t in (q, k, v)]
+    ws = torch.empty(fa.fa_bwd_ex_workspace_bytes(p), dtype=torch.uint8, device="cuda:0")
+    st = fa.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(), l2.data_ptr(), do.data_ptr(),
+                      *(t.data_ptr() for t in g2), p, ws.data_ptr(), ws.numel(), s)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)

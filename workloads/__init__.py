@@ -99,16 +99,19 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def make_inputs(B, Hq, Hkv, S, D, dtype, seed, q_std=1.0, backward=True):
-    """Draw q, k, v (and dO) per the recipe above.  Returns a dict of float32 arrays."""
+def make_inputs(B, Hq, Hkv, S, D, dtype, seed, q_std=1.0, backward=True, Skv=None):
+    """Draw q, k, v (and dO) per the recipe above.  Returns a dict of float32 arrays.
+
+    q and dO are [B,Hq,S,D]; k and v are [B,Hkv,Skv,D] (Skv defaults to S)."""
     if dtype not in DTYPES:
         raise ValueError(f"unknown dtype {dtype!r}")
+    Skv = S if Skv is None else Skv
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, Hq, S, D), dtype=np.float32)
     if q_std != 1.0:
         q *= np.float32(q_std)
-    k = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
-    v = rng.standard_normal((B, Hkv, S, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Skv, D), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Skv, D), dtype=np.float32)
     out = {"q": round_to(q, dtype), "k": round_to(k, dtype), "v": round_to(v, dtype)}
     if backward:
         out["do"] = round_to(rng.standard_normal((B, Hq, S, D), dtype=np.float32), dtype)
@@ -117,3 +120,23 @@ def make_inputs(B, Hq, Hkv, S, D, dtype, seed, q_std=1.0, backward=True):
 
 def workload_inputs(w: Workload):
     return make_inputs(w.B, w.Hq, w.Hkv, w.S, w.D, w.dtype, w.seed, w.q_std, w.backward)
+
+
+def make_varlen_inputs(seqlens_q, seqlens_k, Hq, Hkv, D, dtype, seed, q_std=1.0):
+    """A packed batch: sequence b has seqlens_q[b] query rows and seqlens_k[b] key rows.
+
+    Returns float32 arrays q, dO [Hq,Tq,D], k, v [Hkv,Tk,D] (rows of all
+    sequences back to back within each head) and the int32 offset vectors
+    cu_q, cu_k of length B + 1 (cu[b] is the first row of sequence b)."""
+    if len(seqlens_q) != len(seqlens_k):
+        raise ValueError("one key length per query length")
+    cu_q = np.concatenate([[0], np.cumsum(seqlens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(seqlens_k)]).astype(np.int32)
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((Hq, Tq, D), dtype=np.float32) * np.float32(q_std)
+    k = rng.standard_normal((Hkv, Tk, D), dtype=np.float32)
+    v = rng.standard_normal((Hkv, Tk, D), dtype=np.float32)
+    do = rng.standard_normal((Hq, Tq, D), dtype=np.float32)
+    return {"q": round_to(q, dtype), "k": round_to(k, dtype), "v": round_to(v, dtype),
+            "do": round_to(do, dtype), "cu_q": cu_q, "cu_k": cu_k}
