@@ -125,6 +125,29 @@ __device__ inline vec8<T> acc_to_frag(const f32x16& acc, int base) {
   return f;
 }
 
+// acc + the sum of a fragment's 8 elements, in fp32.  16-bit types use the
+// packed dot product with (1, 1), so the sum is over exactly the rounded
+// values the matrix product consumes.
+__device__ inline float frag_sum(const vec8<__bf16>& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
+}
+__device__ inline float frag_sum(const vec8<_Float16>& f, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
+}
+__device__ inline float frag_sum(const vec8<float>& f, float acc) {
+  return acc + (((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7])));
+}
+
 // Workgroup order for MI355X's 8 XCDs.  The dispatcher hands consecutive
 // workgroup ids to the XCDs round-robin (id % 8), and each XCD has its own L2.
 // Returns the work item a workgroup should take so that XCD x processes the

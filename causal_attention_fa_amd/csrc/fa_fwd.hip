@@ -23,8 +23,8 @@
 //     current tile's math; V^T fragments come from gfx950's LDS transpose read;
 //   * softmax in base 2: p = exp2(s * scale*log2e - m), m tracked in that unit,
 //     and the accumulator is rescaled only when a row's max grows by > 2^4;
-//   * the row sum l is one more MFMA per step (all-ones A operand), so it sums
-//     exactly the rounded P that multiplies V;
+//   * the row sum l is taken over exactly the rounded P that multiplies V
+//     (packed dot products with (1, 1) on the vector ALU);
 //   * causal: workgroups are launched heaviest (last query tiles) first, a wave
 //     skips KV tiles that lie wholly after its rows (or, with a window, wholly
 //     before them), and the element mask is applied on edge tiles only;
@@ -82,13 +82,10 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   f32x16 oacc[HD / 32];
 #pragma unroll
   for (int d = 0; d < HD / 32; ++d) oacc[d] = f32x16{};
-  // Row sums on the matrix cores: an all-ones A operand turns O^T += V^T P^T
-  // into lacc += 1 P^T, whose every register holds sum_kv P~[kv][q] for the
-  // lane's query q (the full sum, both lane halves included).
-  f32x16 lacc = f32x16{};
-  vec8<T> ones;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ones[j] = to_elem<T>(1.f);
+  // Row sum of the rounded P that multiplies V: each lane sums its half of
+  // the tile's keys (packed dot products on the vector ALU, which has slack
+  // beside the matrix cores); the two halves are added at the end.
+  float lsum = 0.f;
   float m = -INFINITY;
 
   // keys the workgroup's rows can see: [lo, hi)
@@ -155,7 +152,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
         const float m_new = fmaxf(m, mx);
         // a row that has seen no key keeps m = -inf and alpha = 1
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-        lacc *= alpha;
+        lsum *= alpha;
 #pragma unroll
         for (int d = 0; d < HD / 32; ++d) oacc[d] *= alpha;
         m = m_new;
@@ -165,13 +162,13 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -ref));
-      // O^T (HD x 32) += V_tile^T P^T ; l += 1^T P^T
+      // O^T (HD x 32) += V_tile^T P^T ; l += sum of the lane's P
 #pragma unroll
       for (int kt = 0; kt < BC / 16; ++kt) {
         const vec8<T> pf = acc_to_frag<T>(s[kt >> 1], 8 * (kt & 1));
 #pragma unroll
         for (int d = 0; d < HD / 32; ++d) oacc[d] = mma<T>(Tile::tr_frag(Vs, kt, 32 * d, lane), pf, oacc[d]);
-        lacc = mma<T>(ones, pf, lacc);
+        lsum = frag_sum(pf, lsum);
       }
     }
     if (more) {
@@ -181,7 +178,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     __syncthreads();
   }
 
-  const float l = lacc[0];
+  const float l = wave_xor32_sum(lsum);
   if (myq < sv.sq) {
     // a row that saw no key has an empty softmax: O = 0, L = -inf
     const float inv = l > 0.f ? 1.f / l : 0.f;
