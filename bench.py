@@ -5,13 +5,18 @@ dQ kernel) over the long-context GQA workload (B=1, Hq=32, Hkv=8, S=16384,
 D=128, bf16, causal) with every input already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--no-memory]
+                    [--no-cpu-baseline] [--no-memory] [--no-decode] [--no-sweep]
 
 Prints one JSON line.  ``value`` is causal fwd+bwd TFLOP/s: 4*D flops per
 visited (query, key) pair for the forward and 10*D for the backward, pairs =
 B*Hq*S*(S+1)/2, divided by the measured time per step.  Per-kernel durations
 come from HIP events the library records around each of its kernel launches
 (fa_profile_events) during the same timed steps.
+
+Also reported, outside the timed steps: ``forward_sweep`` (the forward alone
+at S = 4096, 8192, 16384 with 32/8 heads, D = 128), ``decode`` (one split-KV
+decode step of 16 sequences x 8192 cached keys, as GB/s against HBM, beside
+the plain forward on the same inputs), ``memory`` and ``cpu_baseline``.
 """
 from __future__ import annotations
 
@@ -172,6 +177,117 @@ def run_gpu(w, steps, warmup):
     return total_ms / steps, kernel_ms
 
 
+def _time_calls(fn, steps, warmup, stream, hip, nev=0):
+    """Mean ms of fn(events) over `steps` calls after `warmup`; with nev > 0 each
+    call gets nev fresh events (fa_profile_events) and their gaps are averaged."""
+    import torch
+
+    import causal_attention_fa_amd as fa
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(nev)] for _ in range(steps)] if nev else []
+    arrays = [(ctypes.c_void_p * nev)(*[e.value for e in row]) for row in evs]
+    start, end = hip.event(), hip.event()
+    hip.record(start, stream)
+    for s in range(steps):
+        if nev:
+            fa.fa_profile_events(ctypes.addressof(arrays[s]), nev)
+        fn()
+    fa.fa_profile_events(None, 0)
+    hip.record(end, stream)
+    torch.cuda.synchronize()
+    total = hip.ms(start, end) / steps
+    gaps = [sum(hip.ms(row[i], row[i + 1]) for row in evs) / steps for i in range(nev - 1)] if nev else []
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    hip.destroy(start)
+    hip.destroy(end)
+    return total, gaps
+
+
+def decode_bench(steps, warmup):
+    """One decode step (split-KV forward) of the decode workload, and the plain
+    forward on the same inputs for comparison.  HBM-bound: reported as GB/s of
+    the bytes the step must move (K and V once per KV head, Q, O, L)."""
+    import torch
+
+    import causal_attention_fa_amd as fa
+    from workloads import DECODE, decode_inputs
+    w = DECODE
+    dev = torch.device("cuda:0")
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    code = {"bf16": fa.FA_BF16, "f16": fa.FA_F16, "f32": fa.FA_F32}[w.dtype]
+    t = {n: torch.from_numpy(x).to(dev).to(tdt).contiguous() for n, x in decode_inputs(w).items()}
+    q, k, v = t["q"], t["k"], t["v"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    p = fa.params(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, w.scale, True, None, code)
+    nbytes = fa.fa_fwd_splitkv_workspace_bytes(p, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+    hip = Hip()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
+
+    def split():
+        st = fa.fa_fwd_splitkv(*ptrs, p, 0, ws.data_ptr(), nbytes, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_fwd_splitkv")
+
+    def plain():
+        st = fa.fa_fwd_ex(*ptrs, p, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_fwd_ex")
+
+    ms, (split_ms, merge_ms) = _time_calls(split, steps, warmup, sh, hip, nev=3)
+    plain_ms, _ = _time_calls(plain, steps, warmup, sh, hip)
+    gbs = w.min_bytes() / (ms * 1e-3) / 1e9
+    nsplit = nbytes // (w.B * w.Hq * w.Sq * (w.D + 1) * 4)
+    del t, q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms": round(ms, 4), "split_kernel_ms": round(split_ms, 4),
+            "merge_kernel_ms": round(merge_ms, 4), "num_splits": int(nsplit),
+            "bytes": w.min_bytes(), "achieved": round(gbs, 1), "unit": "GB/s", "bound": "hbm",
+            "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "plain_forward_ms": round(plain_ms, 4), "speedup_vs_plain_forward": round(plain_ms / ms, 2)}
+
+
+def forward_sweep(steps, warmup):
+    """Forward alone at S = 4096, 8192, 16384 (B=1, Hq=32, Hkv=8, D=128, bf16, causal)."""
+    import torch
+
+    import causal_attention_fa_amd as fa
+    out = []
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+    hip = Hip()
+    for S in (4096, 8192, 16384):
+        B, Hq, Hkv, D = 1, 32, 8, 128
+        g = torch.Generator(device=dev).manual_seed(S)
+        q = (3 * torch.randn(B, Hq, S, D, device=dev, generator=g)).to(torch.bfloat16)
+        k = torch.randn(B, Hkv, S, D, device=dev, generator=g).to(torch.bfloat16)
+        v = torch.randn(B, Hkv, S, D, device=dev, generator=g).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        lse = torch.empty(B, Hq, S, device=dev)
+
+        def fwd():
+            st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, S, D,
+                           1 / math.sqrt(D), 1, fa.FA_BF16, sh)
+            if st != fa.FA_OK:
+                raise fa.FAError(st, "fa_fwd")
+
+        ms, _ = _time_calls(fwd, steps, warmup, sh, hip)
+        tf = 4.0 * D * B * Hq * S * (S + 1) / 2 / (ms * 1e-3) / 1e12
+        out.append({"S": S, "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)})
+        del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return {"config": "B=1 Hq=32 Hkv=8 D=128 bf16 causal, forward only", "points": out}
+
+
 def peak_memory(w):
     """Peak device memory of fa fwd+bwd above the inputs, vs materialised [B,Hq,S,S] scores
     (allocator protocol: baseline after inputs, reset peak, run, read peak)."""
@@ -255,6 +371,8 @@ def main():
     ap.add_argument("--workload", default=LONG_CONTEXT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-memory", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over S")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a reference "
                          "dispatch for scaling HBM byte counters); not part of the timed steps")
@@ -339,6 +457,10 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if not args.no_sweep:
+        out["forward_sweep"] = forward_sweep(10, 3)
+    if not args.no_decode:
+        out["decode"] = decode_bench(20, 5)
     if not args.no_memory:
         out["memory"] = [peak_memory(w), peak_memory(WORKLOADS["causal_f16_b1_h8_s4096_d64"])]
     if not args.no_cpu_baseline:

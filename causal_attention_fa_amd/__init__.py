@@ -26,7 +26,8 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FAError", "library_path", "lib",
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_profile_events",
     "fa_params_t", "params", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes",
-    "forward", "backward", "forward_varlen", "backward_varlen",
+    "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
+    "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
@@ -88,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_ex_workspace_bytes.restype = sz
         L.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, pp, vp, sz, vp]
         L.fa_bwd_ex.restype = i
+        L.fa_fwd_splitkv_workspace_bytes.argtypes = [pp, i]
+        L.fa_fwd_splitkv_workspace_bytes.restype = sz
+        L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, pp, i, vp, sz, vp]
+        L.fa_fwd_splitkv.restype = i
         _lib = L
     return _lib
 
@@ -123,6 +128,14 @@ def fa_bwd_ex_workspace_bytes(p) -> int:
 
 def fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, p, workspace, workspace_bytes, stream) -> int:
     return lib().fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, _pp(p), workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_workspace_bytes(p, num_splits=0) -> int:
+    return int(lib().fa_fwd_splitkv_workspace_bytes(_pp(p), num_splits))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, p, num_splits, workspace, workspace_bytes, stream) -> int:
+    return lib().fa_fwd_splitkv(q, k, v, o, lse, _pp(p), num_splits, workspace, workspace_bytes, stream)
 
 
 def fa_status_string(status: int) -> str:
@@ -279,3 +292,29 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     if st != FA_OK:
         raise FAError(st, "fa_bwd_ex")
     return dq, dk, dv
+
+
+def forward_splitkv(q, k, v, scale=None, causal=True, window=None, num_splits=0, cu_seqlens_q=None,
+                    cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, workspace=None):
+    """(o, lse) by the split-KV decode path (fa_fwd_splitkv).
+
+    Dense: q [B,Hq,Sq,D], k, v [B,Hkv,Skv,D].  Packed: q [Hq,total_q,D], k, v
+    [Hkv,total_k,D] with cu_seqlens_* and max_seqlen_* as in ``forward_varlen``.
+    (Hq / Hkv) * Sq must be at most 32; ``num_splits`` <= 0 lets the library choose."""
+    torch = _torch()
+    if cu_seqlens_q is None:
+        B, Hq, Hkv, Sq, Skv, D = _check(q, k, v)
+        p = params(B, Hq, Hkv, Sq, Skv, D, _scale(scale, D), causal, window, _dtype_code(q))
+        lse_shape = (B, Hq, Sq)
+    else:
+        p = _varlen_params(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, window)
+        lse_shape = tuple(q.shape[:2])
+    nbytes = fa_fwd_splitkv_workspace_bytes(p, num_splits)
+    workspace = _workspace(nbytes, workspace, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    st = fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), p, num_splits, workspace.data_ptr(),
+                        workspace.numel(), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_splitkv")
+    return o, lse

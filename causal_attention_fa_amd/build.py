@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 # -amdgpu-mfma-vgpr-form=1: keep MFMA accumulators in architectural VGPRs;

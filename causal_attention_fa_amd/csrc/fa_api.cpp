@@ -63,6 +63,32 @@ fa_status_t check(const fa_params_t* p, fa::Problem* pb, long long* qrows, long 
   return FA_OK;
 }
 
+// Split-KV plan: nsplit key ranges of `chunk` keys (whole split-kernel tiles).
+// With no request, enough ranges to give the GPU about kSplitTarget
+// workgroups, keeping at least two tiles per range.
+constexpr long long kSplitTarget = 512;
+struct SplitPlan {
+  int nsplit, chunk;
+};
+SplitPlan plan_split(const fa_params_t* p, int requested) {
+  const int bc = fa::split_tile_keys(p->dtype);
+  const int ntile = p->Skv > 0 ? (p->Skv + bc - 1) / bc : 1;
+  int ns = requested;
+  if (ns <= 0) {
+    const long long units = (long long)p->B * p->Hkv;
+    const long long want = units > 0 ? (kSplitTarget + units - 1) / units : 1;
+    ns = (int)(want < ntile / 2 ? want : ntile / 2);
+    if (ns < 1) ns = 1;
+  }
+  if (ns > ntile) ns = ntile;
+  const int per = (ntile + ns - 1) / ns;  // tiles per range
+  return SplitPlan{(ntile + per - 1) / per, per * bc};
+}
+
+long long split_work_floats(const fa_params_t* p, const SplitPlan& sp, long long qrows) {
+  return (long long)sp.nsplit * qrows * (p->D + 1);
+}
+
 fa_params_t dense(int B, int Hq, int Hkv, int S, int D, float scale, int causal, fa_dtype_t dtype) {
   fa_params_t p{};
   p.B = B;
@@ -133,6 +159,33 @@ fa_status_t fa_bwd_ex(const void* q, const void* k, const void* v, const void* o
   fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, static_cast<float*>(workspace), pb, p->D, p->scale,
                 (int)p->dtype, g_events, g_nevents};
   return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(const fa_params_t* p, int num_splits) {
+  fa::Problem pb;
+  long long qrows = 0, krows = 0;
+  if (check(p, &pb, &qrows, &krows) != FA_OK || qrows == 0) return 0;
+  if ((long long)(p->Hq / p->Hkv) * p->Sq > 32) return 0;
+  return round256((size_t)split_work_floats(p, plan_split(p, num_splits), qrows) * sizeof(float));
+}
+
+fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, const fa_params_t* p,
+                           int num_splits, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fa::Problem pb;
+  long long qrows = 0, krows = 0;
+  fa_status_t st = check(p, &pb, &qrows, &krows);
+  if (st != FA_OK || qrows == 0) return st;
+  // the query rows of one KV group form one 32-column matrix block
+  if ((long long)(p->Hq / p->Hkv) * p->Sq > 32) return FA_ERR_UNSUPPORTED;
+  if (!present(q) || !present(o) || (lse && !aligned16(lse))) return FA_ERR_INVALID_ARG;
+  if (krows > 0 && (!present(k) || !present(v))) return FA_ERR_INVALID_ARG;
+  if (!present(workspace)) return FA_ERR_INVALID_ARG;
+  const SplitPlan sp = plan_split(p, num_splits);
+  if (workspace_bytes < (size_t)split_work_floats(p, sp, qrows) * sizeof(float)) return FA_ERR_WORKSPACE;
+  fa::SplitArgs a{q,        k,        v,         o,     lse,   static_cast<float*>(workspace),
+                  pb,       p->D,     p->scale,  (int)p->dtype, sp.nsplit, sp.chunk,
+                  qrows,    g_events, g_nevents};
+  return fa::launch_splitkv(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int S,

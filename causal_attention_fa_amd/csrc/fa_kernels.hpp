@@ -46,7 +46,30 @@ struct BwdArgs {
   int nev;
 };
 
+// Split-KV forward: nsplit key ranges of `chunk` keys each (a multiple of
+// split_tile_keys(dtype)); `work` holds nsplit * qrows * (D + 1) fp32 values
+// (partial O rows, then partial L).
+struct SplitArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  float* work;
+  Problem pb;
+  int D;
+  float scale;
+  int dtype;
+  int nsplit;
+  int chunk;
+  long long qrows;
+  hipEvent_t* ev;
+  int nev;
+};
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream);
+int split_tile_keys(int dtype);  // keys per split-kernel tile
 
 }  // namespace fa

@@ -173,12 +173,42 @@ fa_status_t fa_bwd_ex(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Split-KV forward for decode-shaped problems: few query rows per KV head and
+ * many keys, as when decoding against a KV cache.  "Phase 14", section
+ * 已知局限与后续优化方向, asks for a dedicated decode kernel that reduces in
+ * parallel along the keys; "FlashAttention 与 SDPA Backend" names the split-KV
+ * merge as one of a real kernel's choices.  Each sequence's keys are cut into
+ * ranges processed in parallel, each range leaves a normalised partial output
+ * O_s and logsumexp L_s, and a second kernel merges them:
+ * L = log sum_s exp(L_s), O = sum_s exp(L_s - L) O_s.
+ * Same problem, layouts, outputs and errors as fa_fwd_ex, plus:
+ *   num_splits : > 0 chooses the number of key ranges (capped at one per
+ *                key tile of 128 keys, 64 for fp32); <= 0 lets the library
+ *                choose enough ranges to fill the GPU
+ *   workspace  : device scratch of at least
+ *                fa_fwd_splitkv_workspace_bytes(params, num_splits) bytes,
+ *                16-byte aligned, holding the partial results; contents on
+ *                entry are ignored; two calls in flight need two workspaces
+ * FA_ERR_UNSUPPORTED when (Hq / Hkv) * Sq > 32: the query rows of one KV group
+ * share one 32-column matrix block, which is what lets the G heads of a group
+ * read K and V once.  FA_ERR_WORKSPACE when the workspace is too small, and
+ * FA_ERR_INVALID_ARG when it is NULL or misaligned.  Results match fa_fwd_ex's
+ * up to fp32 rounding order and are deterministic for a given split count.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(const fa_params_t* params, int num_splits);
+fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const fa_params_t* params, int num_splits, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Instrumentation for benchmarks (not part of the computation).  After
- * fa_profile_events(ev, n) with ev != NULL, each later fa_fwd / fa_bwd call made
- * from the same host thread records ev[0..] on its stream around every kernel
- * it launches: fa_fwd records ev[0] before and ev[1] after its one kernel;
+ * fa_profile_events(ev, n) with ev != NULL, each later compute call made from
+ * the same host thread records ev[0..] on its stream around every kernel it
+ * launches: fa_fwd records ev[0] before and ev[1] after its one kernel;
  * fa_bwd records ev[0] before the row-dot kernel, ev[1] before the dK/dV
- * kernel, ev[2] before the dQ kernel and ev[3] after it.  Indices >= n are not
+ * kernel, ev[2] before the dQ kernel and ev[3] after it; fa_fwd_splitkv
+ * records ev[0] before its split kernel, ev[1] before its merge kernel and
+ * ev[2] after it (fa_fwd_ex / fa_bwd_ex as fa_fwd / fa_bwd).  Indices >= n are not
  * recorded.  The caller owns the events (created with hipEventCreate) and must
  * keep them alive while in use; fa_profile_events(NULL, 0) turns recording off.
  */

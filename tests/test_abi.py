@@ -26,7 +26,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == ["fa_bwd", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes", "fa_bwd_workspace_bytes", "fa_fwd",
-                     "fa_fwd_ex", "fa_profile_events", "fa_status_string"]
+                     "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_profile_events",
+                     "fa_status_string"]
     L = fa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -230,3 +231,48 @@ def test_ex_backward_without_queries_needs_no_query_buffers():
     p = ex_params(Sq=0)
     assert fa.fa_bwd_ex_workspace_bytes(p) == 0
     assert bwd_ex(p, dk=None) == fa.FA_ERR_INVALID_ARG     # key rows need dk, checked before any launch
+
+
+# ------------------------------------------------------------------ split-KV decode
+
+def splitkv(p=None, num_splits=0, **kw):
+    p = ex_params(Sq=1, Skv=4096) if p is None else p
+    args = dict(q=A, k=A, v=A, o=A, lse=A, workspace=A, workspace_bytes=fa.fa_fwd_splitkv_workspace_bytes(p, num_splits),
+                stream=None)
+    args.update(kw)
+    return fa.fa_fwd_splitkv(args["q"], args["k"], args["v"], args["o"], args["lse"], p, num_splits,
+                             args["workspace"], args["workspace_bytes"], args["stream"])
+
+
+def test_splitkv_workspace_sizing():
+    # 1 x 4 query heads x 1 row, 4096 keys in 128-key tiles: the library picks
+    # min(512 / (B*Hkv), tiles / 2) = 16 ranges; each holds rows x (D + 1) floats
+    p = ex_params(Sq=1, Skv=4096)
+    assert fa.fa_fwd_splitkv_workspace_bytes(p, 0) == 16 * 4 * 65 * 4
+    assert fa.fa_fwd_splitkv_workspace_bytes(p, 3) == 3328     # 3 x 4 x 65 x 4 = 3120, to 256
+    assert fa.fa_fwd_splitkv_workspace_bytes(p, 10 ** 6) == fa.fa_fwd_splitkv_workspace_bytes(p, 32)  # one per tile
+    f32 = ex_params(Sq=1, Skv=4096, dtype=fa.FA_F32)  # 64-key tiles
+    assert fa.fa_fwd_splitkv_workspace_bytes(f32, 10 ** 6) == 64 * 4 * 65 * 4
+    assert fa.fa_fwd_splitkv_workspace_bytes(ex_params(Sq=17, Skv=100), 0) == 0   # 2 x 17 > 32 rows
+    assert fa.fa_fwd_splitkv_workspace_bytes(ex_params(Sq=0), 0) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({"workspace": None}, fa.FA_ERR_INVALID_ARG),
+    ({"workspace": A + 8}, fa.FA_ERR_INVALID_ARG),
+    ({"workspace_bytes": 100}, fa.FA_ERR_WORKSPACE),
+    ({"q": None}, fa.FA_ERR_INVALID_ARG),
+    ({"o": A + 4}, fa.FA_ERR_INVALID_ARG),
+    ({"k": None}, fa.FA_ERR_INVALID_ARG),
+    ({"lse": A + 4}, fa.FA_ERR_INVALID_ARG),
+])
+def test_splitkv_checks(kw, expect):
+    assert splitkv(**kw) == expect
+
+
+def test_splitkv_shape_limits():
+    # group rows beyond one 32-column block
+    assert splitkv(ex_params(Hq=8, Hkv=2, Sq=9, Skv=100), workspace_bytes=1 << 20) == fa.FA_ERR_UNSUPPORTED
+    # no query rows: a no-op that needs no buffers
+    assert splitkv(ex_params(Sq=0), q=None, k=None, v=None, o=None, lse=None, workspace=None) == fa.FA_OK
+    assert splitkv(ex_params(D=96, Sq=1)) == fa.FA_ERR_UNSUPPORTED

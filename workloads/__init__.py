@@ -78,6 +78,46 @@ WORKLOADS = {
     )
 }
 SMALL = "causal_f32_b1_h2_s128_d64"
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Decoding against a KV cache: Sq new query rows per sequence, Skv cached keys,
+    the causal diagonal aligned to the last key (bottom-right)."""
+    name: str
+    dtype: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int
+    D: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def pairs(self) -> int:
+        # query row i of Sq sees keys 0 .. Skv - Sq + i
+        per_head = sum(max(0, min(self.Skv, self.Skv - self.Sq + i + 1)) for i in range(self.Sq))
+        return self.B * self.Hq * per_head
+
+    def flops(self) -> float:
+        return 4.0 * self.D * self.pairs()
+
+    def min_bytes(self) -> int:
+        """Bytes a decode step must move: K, V once per KV head; Q, O; fp32 L."""
+        e = 4 if self.dtype == "f32" else 2
+        kv = 2 * self.B * self.Hkv * self.Skv * self.D * e
+        qo = 2 * self.B * self.Hq * self.Sq * self.D * e
+        return kv + qo + 4 * self.B * self.Hq * self.Sq
+
+
+# One decode step of the Qwen3-style GQA shape (32 query heads over 8 KV heads,
+# head dim 128) for a batch of 16 sequences with 8192 cached keys each.
+DECODE = DecodeWorkload("decode_qwen3_gqa_bf16_b16_h32kv8_sq1_skv8192_d128", "bf16", 16, 32, 8, 1, 8192, 128,
+                        seed=5)
 LONG_CONTEXT = "longctx_gqa_causal_bf16_b1_h32kv8_s16384_d128"
 
 
@@ -140,3 +180,7 @@ def make_varlen_inputs(seqlens_q, seqlens_k, Hq, Hkv, D, dtype, seed, q_std=1.0)
     do = rng.standard_normal((Hq, Tq, D), dtype=np.float32)
     return {"q": round_to(q, dtype), "k": round_to(k, dtype), "v": round_to(v, dtype),
             "do": round_to(do, dtype), "cu_q": cu_q, "cu_k": cu_k}
+
+
+def decode_inputs(w: DecodeWorkload):
+    return make_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.D, w.dtype, w.seed, backward=False, Skv=w.Skv)
