@@ -314,35 +314,39 @@ struct TileLoader<T, ROWS, HD, NT, true> {
   static constexpr int kNW = NT / 64;
   static constexpr int kRowBytes = HD * 2;
   static constexpr int kInstr = ROWS * kRowBytes / (kNW * 1024);
+  static constexpr int kRowsPerInstr = kNW * 1024 / kRowBytes;  // tile rows one instruction of all waves covers
   static_assert(ROWS * kRowBytes % (kNW * 1024) == 0, "tile must be whole 1 KiB wave slices");
-  int off[kInstr];  // element offset (row * HD + logical column) this lane loads, per instruction
-  int wslot;        // wave index (uniform)
+  // The swizzle reads row bits 0..3 only, so with a multiple of 16 rows per
+  // instruction a lane loads the same (swizzled) column in every instruction
+  // and only its row advances: one 32-bit offset per lane serves them all,
+  // and the per-instruction step is uniform.
+  static_assert(kRowsPerInstr % 16 == 0, "per-instruction row step must keep the swizzle");
+  uint32_t col;  // byte offset of this lane's logical 16-byte chunk within its row
+  int row;       // tile row this lane loads in instruction 0
+  int wslot;     // wave index (uniform)
 
   __device__ inline void init(int tid) {
     wslot = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-#pragma unroll
-    for (int p = 0; p < kInstr; ++p) {
-      const int byte = (p * kNW + wslot) * 1024 + 16 * lane;
-      const int row = byte / kRowBytes;
-      const int pch = (byte % kRowBytes) / 16;
-      off[p] = row * HD + (pch ^ Tile::swz(row)) * 8;
-    }
+    const int byte = wslot * 1024 + 16 * (tid & 63);
+    row = byte / kRowBytes;
+    const int pch = (byte % kRowBytes) / 16;
+    col = (uint32_t)((pch ^ Tile::swz(row)) * 16);
   }
   __device__ inline void issue(const T* __restrict__ g, int row0, int nvalid, T* lds, int) {
     if (row0 + ROWS <= nvalid) {
-      const T* gb = g + (size_t)row0 * HD;
+      // uniform base (scalar registers) + one per-lane 32-bit offset
+      const char* gb = reinterpret_cast<const char*>(g + (size_t)row0 * HD);
+      const uint32_t off = (uint32_t)(row * kRowBytes) + col;
 #pragma unroll
       for (int p = 0; p < kInstr; ++p)
-        __builtin_amdgcn_global_load_lds((const void*)(gb + off[p]),
+        __builtin_amdgcn_global_load_lds((const void*)(gb + (size_t)p * kRowsPerInstr * kRowBytes + off),
                                          (__attribute__((address_space(3))) void*)(lds + (p * kNW + wslot) * 512),
                                          16, 0, 0);
     } else {
 #pragma unroll
       for (int p = 0; p < kInstr; ++p) {
-        const int r = off[p] / HD;
-        const int row = min(row0 + r, nvalid - 1);
-        __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)row * HD + (off[p] - r * HD)),
+        const int r = min(row0 + row + p * kRowsPerInstr, nvalid - 1);
+        __builtin_amdgcn_global_load_lds((const void*)(reinterpret_cast<const char*>(g) + (size_t)r * kRowBytes + col),
                                          (__attribute__((address_space(3))) void*)(lds + (p * kNW + wslot) * 512),
                                          16, 0, 0);
       }

@@ -53,7 +53,12 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   constexpr int NT = NW * 64;
   using Tile = RowTile<T, BC, HD>;
   constexpr int kBuf = 2 * Tile::kElems;  // K tile, then V tile
-  __shared__ __attribute__((aligned(16))) T lds[2 * kBuf];
+  // Two buffers as two LDS variables, and the tile loop unrolled by two so
+  // every access names its buffer: the compiler then knows that the direct
+  // loads filling one buffer cannot alias the transpose reads of the other
+  // and does not wait for those loads before reading V.
+  __shared__ __attribute__((aligned(16))) T lds_a[kBuf];
+  __shared__ __attribute__((aligned(16))) T lds_b[kBuf];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
@@ -99,35 +104,36 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   kld.init(tid);
   vld.init(tid);
   if (ntiles > 0) {
-    kld.issue(Kh, jt0 * BC, sv.skv, lds, tid);
-    vld.issue(Vh, jt0 * BC, sv.skv, lds + Tile::kElems, tid);
+    kld.issue(Kh, jt0 * BC, sv.skv, lds_a, tid);
+    vld.issue(Vh, jt0 * BC, sv.skv, lds_a + Tile::kElems, tid);
     kld.land(tid);
     vld.land(tid);
   }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // one KV tile: compute on `cur` while the next tile streams into `nxt`
+  auto tile = [&](const int it, const T* cur, T* nxt) __attribute__((always_inline)) {
     const int j0 = (jt0 + it) * BC;
     const bool more = it + 1 < ntiles;
     if (more) {  // the other buffer was last read before the previous barrier
-      T* nb = lds + ((it + 1) & 1) * kBuf;
-      kld.issue(Kh, j0 + BC, sv.skv, nb, tid);
-      vld.issue(Vh, j0 + BC, sv.skv, nb + Tile::kElems, tid);
+      kld.issue(Kh, j0 + BC, sv.skv, nxt, tid);
+      vld.issue(Vh, j0 + BC, sv.skv, nxt + Tile::kElems, tid);
     }
-    const T* Ks = lds + (it & 1) * kBuf;
+    const T* Ks = cur;
     const T* Vs = Ks + Tile::kElems;
     // does any of this wave's rows see a key of the tile?
     const bool active = (!CAUSAL || j0 <= qw0 + 31 + off) &&
                         (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
     if (active) {
-      // S^T (BC x 32) = K_tile Q_w^T
+      // S^T (BC x 32) = K_tile Q_w^T; the key blocks' accumulation chains are
+      // interleaved so each pair of LDS reads feeds two independent products
       f32x16 s[BC / 32];
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        s[kb] = f32x16{};
+      for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
 #pragma unroll
-        for (int t = 0; t < HD / 16; ++t) s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
-      }
+      for (int t = 0; t < HD / 16; ++t)
+#pragma unroll
+        for (int kb = 0; kb < BC / 32; ++kb) s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
       // invisible keys (causal / window / past the end) get -inf
       const bool edge = (CAUSAL && j0 + BC - 1 > qw0 + off) ||
                         (WINDOW && j0 < qw0 + 31 + off - pb.window) || (j0 + BC > sv.skv);
@@ -176,6 +182,10 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       vld.land(tid);
     }
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    tile(it, lds_a, lds_b);
+    if (it + 1 < ntiles) tile(it + 1, lds_b, lds_a);
   }
 
   const float l = wave_xor32_sum(lsum);
