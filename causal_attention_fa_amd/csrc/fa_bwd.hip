@@ -143,13 +143,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
       ++hq;
     }
   };
+  // a head's first query row, from the group's first head (no offset loads)
+  const size_t hstride = q_head_stride(pb);
   auto issue = [&](int hq, int i0, int buf) {
-    const Seq sq = seq_of(pb, b, hq, hkv);
+    const size_t q_row0 = sv0.q_row0 + (size_t)(hq - hkv * G) * hstride;
     T* base = lds + buf * kElems;
-    qld.issue(Q + sq.q_row0 * HD, i0, sq.sq, base + kOffQ, tid);
-    dold.issue(dO + sq.q_row0 * HD, i0, sq.sq, base + kOffD, tid);
+    qld.issue(Q + q_row0 * HD, i0, sv0.sq, base + kOffQ, tid);
+    dold.issue(dO + q_row0 * HD, i0, sv0.sq, base + kOffD, tid);
     if (tid < BQ) {
-      const size_t row = sq.q_row0 + min(i0 + tid, sq.sq - 1);
+      const size_t row = q_row0 + min(i0 + tid, sv0.sq - 1);
       ld_l = LSE[row] * kLog2e;
       ld_d = Dd[row];
     }

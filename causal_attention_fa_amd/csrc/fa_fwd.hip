@@ -126,7 +126,8 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
                         (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
     if (active) {
       // S^T (BC x 32) = K_tile Q_w^T; the key blocks' accumulation chains are
-      // interleaved so each pair of LDS reads feeds two independent products
+      // interleaved so each pair of LDS reads feeds two independent products,
+      // and each step's reads are issued one step ahead of its products
       f32x16 s[BC / 32];
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
@@ -134,6 +135,17 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       for (int t = 0; t < HD / 16; ++t)
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb) s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
+      if constexpr (sizeof(T) == 2) {
+        // order: the fragments of step t+1 are read before the products of
+        // step t (one 16-byte LDS read and one product per fragment)
+        __builtin_amdgcn_sched_group_barrier(0x100, BC / 32, 0);  // LDS reads
+#pragma unroll
+        for (int t = 0; t < HD / 16 - 1; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x100, BC / 32, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, BC / 32, 0);  // matrix products
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, BC / 32, 0);
+      }
       // invisible keys (causal / window / past the end) get -inf
       const bool edge = (CAUSAL && j0 + BC - 1 > qw0 + off) ||
                         (WINDOW && j0 < qw0 + 31 + off - pb.window) || (j0 + BC > sv.skv);

@@ -50,6 +50,10 @@ __device__ inline Seq seq_of(const Problem& p, int b, int hq, int hkv) {
   return s;
 }
 
+// Distance in rows between the first query rows of heads hq and hq + 1 of
+// one sequence (the query layouts' head stride).
+__device__ inline size_t q_head_stride(const Problem& p) { return p.cu_q != nullptr ? (size_t)p.Tq : (size_t)p.Sq; }
+
 // Visibility of key j to query i (both relative to their sequence); the mask
 // kinds are compile-time so the common causal-only path carries no window.
 template <bool CAUSAL, bool WINDOW>
