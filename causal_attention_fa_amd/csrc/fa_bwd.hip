@@ -381,6 +381,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
 }
 
 // ------------------------------------------------------------------ launch
+template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW>
+static void launch_dq_nw(const BwdArgs& a, hipStream_t st, float c) {
+  constexpr int BC = 64;
+  const Problem& pb = a.pb;
+  const int nqt = (pb.Sq + 32 * NW - 1) / (32 * NW);
+  dim3 grid(nqt * pb.B * pb.Hq);
+  if (grid.x > 0)
+    hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL, WINDOW>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
+                       (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dq, pb, c,
+                       a.scale, nqt);
+}
+
 template <typename T, int HD, bool CAUSAL, bool WINDOW>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const Problem& pb = a.pb;
@@ -407,18 +419,14 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
-    constexpr int NW = 4, BC = 64;
-    const int nqt = (pb.Sq + 32 * NW - 1) / (32 * NW);
-    dim3 grid(nqt * pb.B * pb.Hq);
-    mark(a.ev, a.nev, 2, st);
-    if (grid.x > 0)
-      hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL, WINDOW>), grid, dim3(NW * 64), 0, st, (const T*)a.q, (const T*)a.k,
-                         (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dq, pb, c, a.scale,
-                         nqt);
-    mark(a.ev, a.nev, 3, st);
-    return hipGetLastError();
-  }
+  mark(a.ev, a.nev, 2, st);
+  // dQ: 8-wave workgroups when there are enough of them (as the forward)
+  if (sizeof(T) == 2 && (long long)((pb.Sq + 255) / 256) * pb.B * pb.Hq >= kWideGrid)
+    launch_dq_nw<T, HD, 8, CAUSAL, WINDOW>(a, st, c);
+  else
+    launch_dq_nw<T, HD, 4, CAUSAL, WINDOW>(a, st, c);
+  mark(a.ev, a.nev, 3, st);
+  return hipGetLastError();
 }
 
 template <typename T, int HD>

@@ -215,15 +215,26 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   }
 }
 
-template <typename T, int HD, bool CAUSAL, bool WINDOW>
-static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
-  constexpr int NW = 4, BC = 64, BR = 32 * NW;
+template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW>
+static void launch_fwd_nw(const FwdArgs& a, hipStream_t st) {
+  constexpr int BC = 64, BR = 32 * NW;
   const int nqt = (a.pb.Sq + BR - 1) / BR;
   dim3 grid(nqt * a.pb.B * a.pb.Hq), block(NW * 64);
-  mark(a.ev, a.nev, 0, st);
   if (grid.x > 0)
     hipLaunchKernelGGL((fwd_kernel<T, HD, BC, NW, CAUSAL, WINDOW>), grid, block, 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.pb, a.scale * kLog2e, nqt);
+}
+
+template <typename T, int HD, bool CAUSAL, bool WINDOW>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
+  mark(a.ev, a.nev, 0, st);
+  // 16-bit: workgroups of 8 waves (256 query rows) share each K/V tile among
+  // twice the waves, which is faster when there are enough of them to fill
+  // the GPU several times over (one such workgroup fits a CU at a time)
+  if (sizeof(T) == 2 && (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq >= kWideGrid)
+    launch_fwd_nw<T, HD, 8, CAUSAL, WINDOW>(a, st);
+  else
+    launch_fwd_nw<T, HD, 4, CAUSAL, WINDOW>(a, st);
   mark(a.ev, a.nev, 1, st);
   return hipGetLastError();
 }

@@ -22,6 +22,10 @@ struct FwdArgs {
   int nev;
 };
 
+// Grids of at least this many 8-wave workgroups (8 per CU) run the forward
+// and dQ kernels with 8 waves per workgroup; smaller ones use 4.
+constexpr long long kWideGrid = 2048;
+
 // Records ev[i] on the stream when instrumentation asked for it.
 inline void mark(hipEvent_t* ev, int nev, int i, hipStream_t st) {
   if (ev != nullptr && i < nev) (void)hipEventRecord(ev[i], st);

@@ -212,3 +212,27 @@ def test_equal_lengths_ex_matches_plain_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal,window", [(False, None), (True, 300), (False, 700)])
+def test_wide_grid_masks(causal, window):
+    """A grid large enough for the 8-wave workgroups of the forward and dQ kernels
+    (B=8, 32/8 heads, S=2048, D=128, bf16) with the non-causal and windowed masks:
+    sampled rows of every head against the oracle, and one whole KV group's gradients."""
+    B, Hq, Hkv, S, D, dtype = 8, 32, 8, 2048, 128, "bf16"
+    scale = 1.0 / math.sqrt(D)
+    inp = make_inputs(B, Hq, Hkv, S, D, dtype, seed=4200 + (window or 0), q_std=2.0)
+    what = f"wide grid causal={causal} window={window}"
+    say("case", what)
+    o, lse, (dq, dk, dv) = run_dense(inp, dtype, scale, causal, window)
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, S - 1], rng.integers(0, S, 5)]))
+    for b in (0, 7):
+        for h in range(0, Hq, 5):
+            Or, Lr = oracle.sdpa_forward_rows(inp["q"], inp["k"], inp["v"], scale, causal, b, h, rows, window=window)
+            check_o(o[b, h, rows], Or, dtype, f"{what} b={b} h={h}")
+            check_lse(lse[b, h, rows], Lr, dtype, f"{what} b={b} h={h}")
+    g = oracle.sdpa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, groups=[(3, 5)], window=window)
+    heads = list(range(5 * 4, 6 * 4))
+    check_o(o[3, heads], g["o"][3, heads], dtype, what + " group")
+    check_grads((dq[3, heads], dk[3, 5], dv[3, 5]), (g["dq"][3, heads], g["dk"][3, 5], g["dv"][3, 5]), dtype, what)
