@@ -127,7 +127,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   const int per_head = nqt - first;
   const int total = G * per_head;
 
-  TileLoader<T, BQ, HD, NT> qld, dold;
+  LoopLoader<T, BQ, HD, NT> qld, dold;
   qld.init(tid);
   dold.init(tid);
   float ld_l = 0.f, ld_d = 0.f;
@@ -145,22 +145,23 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   };
   // a head's first query row, from the group's first head (no offset loads)
   const size_t hstride = q_head_stride(pb);
+  // L and D of the tile's rows: every lane loads one (lanes past BQ repeat a
+  // row), outside any branch and scaled only at commit, so nothing waits for
+  // them (or, behind them, for the tile's loads) before the tile is needed
   auto issue = [&](int hq, int i0, int buf) {
     const size_t q_row0 = sv0.q_row0 + (size_t)(hq - hkv * G) * hstride;
+    const size_t row = q_row0 + min(i0 + (tid & (BQ - 1)), sv0.sq - 1);
+    ld_l = LSE[row];
+    ld_d = Dd[row];
     T* base = lds + buf * kElems;
     qld.issue(Q + q_row0 * HD, i0, sv0.sq, base + kOffQ, tid);
     dold.issue(dO + q_row0 * HD, i0, sv0.sq, base + kOffD, tid);
-    if (tid < BQ) {
-      const size_t row = q_row0 + min(i0 + tid, sv0.sq - 1);
-      ld_l = LSE[row] * kLog2e;
-      ld_d = Dd[row];
-    }
   };
   auto commit = [&](int buf) {
     qld.land(tid);
     dold.land(tid);
     if (tid < BQ) {
-      lds_ld[buf][0][tid] = ld_l;
+      lds_ld[buf][0][tid] = ld_l * kLog2e;
       lds_ld[buf][1][tid] = ld_d;
     }
   };

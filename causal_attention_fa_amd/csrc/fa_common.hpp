@@ -16,6 +16,8 @@
 // forms one 2-deep product), so fp32 inputs are multiplied in true fp32.
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -354,6 +356,62 @@ struct TileLoader<T, ROWS, HD, NT, true> {
   }
   __device__ inline void land(int) {}
 };
+
+// The direct loads of TileLoader written as inline assembly.  The compiler
+// makes an LDS read wait for every direct load still in flight unless it can
+// prove the two do not overlap, which it cannot when a kernel picks its
+// double buffer at run time (or reads other LDS tiles besides).  It does not
+// see these loads at all, so reads of the current buffer overlap the loads
+// into the other one.  land() waits for them explicitly (vector memory
+// completes in order, so a wait the compiler places for any load issued
+// after them covers them too); the caller's barrier then publishes the tile.
+// Used where it measured faster: the dK / dV kernel's query-tile stream.
+template <typename T, int ROWS, int HD, int NT>
+struct AsmTileLoader : TileLoader<T, ROWS, HD, NT, true> {
+  using Base = TileLoader<T, ROWS, HD, NT, true>;
+  using Base::col;
+  using Base::row;
+  using Base::wslot;
+  static constexpr int kNW = Base::kNW, kInstr = Base::kInstr, kRowBytes = Base::kRowBytes;
+  static constexpr int kRowsPerInstr = Base::kRowsPerInstr;
+
+  // LDS byte address of this wave's 1 KiB slice of instruction p (uniform)
+  __device__ static inline uint32_t slice(T* lds, int p, int w) {
+    const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)lds);
+    return __builtin_amdgcn_readfirstlane(base + (uint32_t)((p * kNW + w) * 1024));
+  }
+  __device__ inline void issue(const T* g, int row0, int nvalid, T* lds, int) {
+    if (row0 + ROWS <= nvalid) {
+      const char* gb = reinterpret_cast<const char*>(g + (size_t)row0 * HD);
+      const uint32_t off = (uint32_t)(row * kRowBytes) + col;
+#pragma unroll
+      for (int p = 0; p < kInstr; ++p) {
+        const char* src = gb + (size_t)p * kRowsPerInstr * kRowBytes;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(slice(lds, p, wslot)), "v"(off), "s"(src)
+                     : "memory", "m0");
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < kInstr; ++p) {
+        const int r = min(row0 + row + p * kRowsPerInstr, nvalid - 1);
+        const char* src = reinterpret_cast<const char*>(g) + (size_t)r * kRowBytes + col;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(slice(lds, p, wslot)), "v"(src)
+                     : "memory", "m0");
+      }
+    }
+  }
+  __device__ inline void land(int) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+};
+
+// Loader for tiles streamed inside a loop: the assembly form for 16-bit
+// elements, register staging for fp32.
+template <typename T, int ROWS, int HD, int NT>
+using LoopLoader = typename std::conditional<sizeof(T) == 2, AsmTileLoader<T, ROWS, HD, NT>,
+                                             TileLoader<T, ROWS, HD, NT>>::type;
 
 // Stores 4 consecutive output elements (fp32 values) at p.
 template <typename T>
