@@ -197,6 +197,16 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
           dp[qb] = mma<T>(Tile::frag(dOs, 32 * qb + r, 16 * t, h), VTile::frag(lds_v, 32 * w + r, 16 * t, h),
                           dp[qb]);
         }
+        if constexpr (sizeof(T) == 2) {
+          // the Q, dO and V fragments of step t+1 are read before the products of step t
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads
+#pragma unroll
+          for (int t = 0; t < HD / 16 - 1; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // matrix products
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
       }
       // invisible (query, key) pairs and queries past the end get p = 0 (keys
       // past the end only feed dK / dV columns that are never stored)
@@ -342,6 +352,16 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
         for (int t = 0; t < HD / 16; ++t) {
           s = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s);
           dp = mma<T>(Tile::frag(Vs, 32 * kb + r, 16 * t, h), df[t], dp);
+        }
+        if constexpr (sizeof(T) == 2) {
+          // the K and V fragments of step t+1 are read before the products of step t
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+#pragma unroll
+          for (int t = 0; t < HD / 16 - 1; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // matrix products
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
