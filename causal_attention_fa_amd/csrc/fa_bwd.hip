@@ -317,7 +317,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   const int jt0 = lo / BC;
   const int ntiles = hi > lo ? (hi + BC - 1) / BC - jt0 : 0;
 
-  TileLoader<T, BC, HD, NT> kld, vld;
+  LoopLoader<T, BC, HD, NT> kld, vld;
   kld.init(tid);
   vld.init(tid);
   if (ntiles > 0) {
@@ -327,6 +327,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     vld.land(tid);
   }
   __syncthreads();
+  // Everything issued so far has landed; a wait the compiler sees tells it
+  // so, and it then places no waits for these loads inside the loop, where
+  // they would also wait for the loop's own assembly loads.
+  __builtin_amdgcn_s_waitcnt(0);
 
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = (jt0 + it) * BC;

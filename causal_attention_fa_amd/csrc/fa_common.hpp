@@ -162,8 +162,20 @@ __device__ inline int xcd_slice(int id, int n) {
   return (id & 7) * per + (id >> 3);
 }
 
-__device__ inline float wave_xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ inline float wave_xor32_sum(float x) { return x + __shfl_xor(x, 32); }
+// Combine a value with the one in lane l ^ 32: gfx950's permlane32 swap
+// exchanges the two wave halves in registers (no LDS round trip).
+__device__ inline float2 wave_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float wave_xor32_max(float x) {
+  const float2 p = wave_halves(x);
+  return fmaxf(p.x, p.y);
+}
+__device__ inline float wave_xor32_sum(float x) {
+  const float2 p = wave_halves(x);
+  return p.x + p.y;
+}
 
 // ------------------------------------------------------------------ LDS tiles
 // Row tile: ROWS x HD elements, row-major.
@@ -357,15 +369,22 @@ struct TileLoader<T, ROWS, HD, NT, true> {
   __device__ inline void land(int) {}
 };
 
-// The direct loads of TileLoader written as inline assembly.  The compiler
-// makes an LDS read wait for every direct load still in flight unless it can
-// prove the two do not overlap, which it cannot when a kernel picks its
-// double buffer at run time (or reads other LDS tiles besides).  It does not
-// see these loads at all, so reads of the current buffer overlap the loads
-// into the other one.  land() waits for them explicitly (vector memory
-// completes in order, so a wait the compiler places for any load issued
-// after them covers them too); the caller's barrier then publishes the tile.
-// Used where it measured faster: the dK / dV kernel's query-tile stream.
+// The direct loads of TileLoader written as inline assembly, for tiles
+// streamed inside a loop.  Seen by the compiler, direct loads cost twice:
+//   * it makes an LDS read wait for every direct load still in flight unless
+//     it can prove the two do not overlap, which it cannot when a kernel
+//     picks its double buffer at run time (or reads other LDS tiles besides);
+//   * with a direct load in a loop it no longer counts LDS reads one by one:
+//     every wait for a fragment waits for all reads in flight, which undoes
+//     reading fragments ahead of their products.
+// It does not see these loads at all, so neither happens.  land() waits for
+// them explicitly (vector memory completes in order, so a wait the compiler
+// places for any load issued after them covers them too); the caller's
+// barrier then publishes the tile.  The flip side: a wait the compiler places
+// for a load issued before the loop (say, a fragment kept in registers)
+// counts as if these loads did not exist, so it would also wait for them.
+// Kernels therefore make every earlier load land before the loop with a wait
+// the compiler sees (__builtin_amdgcn_s_waitcnt(0)).
 template <typename T, int ROWS, int HD, int NT>
 struct AsmTileLoader : TileLoader<T, ROWS, HD, NT, true> {
   using Base = TileLoader<T, ROWS, HD, NT, true>;

@@ -19,8 +19,11 @@
 //     operand of O^T += V^T P^T (no LDS round trip for P);
 //   * Q stays in registers (B operand of S^T) for the whole kernel;
 //   * K and V tiles are staged row-major (XOR-swizzled) in LDS, double
-//     buffered: the next tile's direct global->LDS loads are issued before the
-//     current tile's math; V^T fragments come from gfx950's LDS transpose read;
+//     buffered: the next stage's direct global->LDS loads are issued before
+//     the current stage's math; V^T fragments come from gfx950's LDS
+//     transpose read.  A stage is 128 keys (two 64-key tiles) for 8-wave
+//     workgroups, which have the CU's LDS to themselves, and one tile
+//     otherwise; the waves synchronise once per stage;
 //   * softmax in base 2: p = exp2(s * scale*log2e - m), m tracked in that unit,
 //     and the accumulator is rescaled only when a row's max grows by > 2^4;
 //   * the row sum l is taken over exactly the rounded P that multiplies V
@@ -45,18 +48,19 @@ namespace fa {
 // long-context workload), while 2^8 with an unrounded l does not.
 constexpr float kRescaleLog2 = 4.f;
 
-template <typename T, int HD, int BC, int NW, bool CAUSAL, bool WINDOW>
+template <typename T, int HD, int BC, int BS, int NW, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, Problem pb, float c, int nqt) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
-  using Tile = RowTile<T, BC, HD>;
-  constexpr int kBuf = 2 * Tile::kElems;  // K tile, then V tile
-  // Two buffers as two LDS variables, and the tile loop unrolled by two so
-  // every access names its buffer: the compiler then knows that the direct
-  // loads filling one buffer cannot alias the transpose reads of the other
-  // and does not wait for those loads before reading V.
+  using Tile = RowTile<T, BC, HD>;   // the unit of the products: BC keys
+  using Stage = RowTile<T, BS, HD>;  // the unit of the loads and barriers: BS keys
+  constexpr int kSub = BS / BC;
+  static_assert(BS % BC == 0 && BC % 16 == 0, "a stage is whole tiles; the swizzle repeats every 16 rows");
+  constexpr int kBuf = 2 * Stage::kElems;  // K stage, then V stage
+  // Two buffers as two LDS variables, and the stage loop unrolled by two, so
+  // that every LDS address is a register plus a constant offset.
   __shared__ __attribute__((aligned(16))) T lds_a[kBuf];
   __shared__ __attribute__((aligned(16))) T lds_b[kBuf];
 
@@ -97,96 +101,106 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   const int last = min(i0 + BR, sv.sq) - 1;
   const int hi = CAUSAL ? min(sv.skv, last + off + 1) : sv.skv;
   const int lo = WINDOW ? max(0, i0 + off - pb.window) : 0;
-  const int jt0 = lo / BC;
-  const int ntiles = hi > lo ? (hi + BC - 1) / BC - jt0 : 0;
+  const int jt0 = lo / BS;
+  const int nstages = hi > lo ? (hi + BS - 1) / BS - jt0 : 0;
 
-  TileLoader<T, BC, HD, NT> kld, vld;
+  LoopLoader<T, BS, HD, NT> kld, vld;
   kld.init(tid);
   vld.init(tid);
-  if (ntiles > 0) {
-    kld.issue(Kh, jt0 * BC, sv.skv, lds_a, tid);
-    vld.issue(Vh, jt0 * BC, sv.skv, lds_a + Tile::kElems, tid);
+  if (nstages > 0) {
+    kld.issue(Kh, jt0 * BS, sv.skv, lds_a, tid);
+    vld.issue(Vh, jt0 * BS, sv.skv, lds_a + Stage::kElems, tid);
     kld.land(tid);
     vld.land(tid);
   }
   __syncthreads();
+  // Q has landed too (the loads above waited for it): a wait the compiler
+  // sees says so, and it then places no waits for Q inside the loop, where
+  // they would also wait for the loop's own assembly loads.
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // one KV tile: compute on `cur` while the next tile streams into `nxt`
-  auto tile = [&](const int it, const T* cur, T* nxt) __attribute__((always_inline)) {
-    const int j0 = (jt0 + it) * BC;
-    const bool more = it + 1 < ntiles;
+  // one KV stage: compute on `cur` while the next stage streams into `nxt`.
+  // The waves synchronise once per stage; within it each wave runs through
+  // the stage's tiles at its own pace.
+  auto stage = [&](const int it, const T* cur, T* nxt) __attribute__((always_inline)) {
+    const int s0 = (jt0 + it) * BS;
+    const bool more = it + 1 < nstages;
     if (more) {  // the other buffer was last read before the previous barrier
-      kld.issue(Kh, j0 + BC, sv.skv, nxt, tid);
-      vld.issue(Vh, j0 + BC, sv.skv, nxt + Tile::kElems, tid);
+      kld.issue(Kh, s0 + BS, sv.skv, nxt, tid);
+      vld.issue(Vh, s0 + BS, sv.skv, nxt + Stage::kElems, tid);
     }
-    const T* Ks = cur;
-    const T* Vs = Ks + Tile::kElems;
-    // does any of this wave's rows see a key of the tile?
-    const bool active = (!CAUSAL || j0 <= qw0 + 31 + off) &&
-                        (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
-    if (active) {
-      // S^T (BC x 32) = K_tile Q_w^T; the key blocks' accumulation chains are
-      // interleaved so each pair of LDS reads feeds two independent products,
-      // and each step's reads are issued one step ahead of its products
-      f32x16 s[BC / 32];
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int j0 = s0 + sub * BC;
+      const T* Ks = cur + sub * Tile::kElems;
+      const T* Vs = cur + Stage::kElems + sub * Tile::kElems;
+      // does any of this wave's rows see a key of the tile?
+      const bool active = j0 < hi && (!CAUSAL || j0 <= qw0 + 31 + off) &&
+                          (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
+      if (active) {
+        // S^T (BC x 32) = K_tile Q_w^T; the key blocks' accumulation chains are
+        // interleaved so each pair of LDS reads feeds two independent products,
+        // and each step's reads are issued one step ahead of its products
+        f32x16 s[BC / 32];
 #pragma unroll
-      for (int t = 0; t < HD / 16; ++t)
+        for (int kb = 0; kb < BC / 32; ++kb) s[kb] = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb) s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
-      if constexpr (sizeof(T) == 2) {
-        // order: the fragments of step t+1 are read before the products of
-        // step t (one 16-byte LDS read and one product per fragment)
-        __builtin_amdgcn_sched_group_barrier(0x100, BC / 32, 0);  // LDS reads
+        for (int t = 0; t < HD / 16; ++t)
 #pragma unroll
-        for (int t = 0; t < HD / 16 - 1; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x100, BC / 32, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, BC / 32, 0);  // matrix products
+          for (int kb = 0; kb < BC / 32; ++kb) s[kb] = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s[kb]);
+        if constexpr (sizeof(T) == 2) {
+          // order: the fragments of step t+1 are read before the products of
+          // step t (one 16-byte LDS read and one product per fragment)
+          __builtin_amdgcn_sched_group_barrier(0x100, BC / 32, 0);  // LDS reads
+#pragma unroll
+          for (int t = 0; t < HD / 16 - 1; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x100, BC / 32, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, BC / 32, 0);  // matrix products
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, BC / 32, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, BC / 32, 0);
-      }
-      // invisible keys (causal / window / past the end) get -inf
-      const bool edge = (CAUSAL && j0 + BC - 1 > qw0 + off) ||
-                        (WINDOW && j0 < qw0 + 31 + off - pb.window) || (j0 + BC > sv.skv);
-      if (edge) {
+        // invisible keys (causal / window / past the end) get -inf
+        const bool edge = (CAUSAL && j0 + BC - 1 > qw0 + off) ||
+                          (WINDOW && j0 < qw0 + 31 + off - pb.window) || (j0 + BC > sv.skv);
+        if (edge) {
+#pragma unroll
+          for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+              s[kb][i] = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? s[kb][i] : -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            s[kb][i] = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? s[kb][i] : -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = wave_xor32_max(mx) * c;
+        // Move the reference only when a row's max outgrows it by 2^4 (any lane:
+        // the branch is wave-uniform).  O = acc / l is exact for any reference.
+        if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
+          const float m_new = fmaxf(m, mx);
+          // a row that has seen no key keeps m = -inf and alpha = 1
+          const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+          lsum *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+          for (int d = 0; d < HD / 32; ++d) oacc[d] *= alpha;
+          m = m_new;
+        }
+        const float ref = (m == -INFINITY) ? 0.f : m;  // a row with no key yet keeps p = 0
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = wave_xor32_max(mx) * c;
-      // Move the reference only when a row's max outgrows it by 2^4 (any lane:
-      // the branch is wave-uniform).  O = acc / l is exact for any reference.
-      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
-        const float m_new = fmaxf(m, mx);
-        // a row that has seen no key keeps m = -inf and alpha = 1
-        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-        lsum *= alpha;
+        for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-        for (int d = 0; d < HD / 32; ++d) oacc[d] *= alpha;
-        m = m_new;
-      }
-      const float ref = (m == -INFINITY) ? 0.f : m;  // a row with no key yet keeps p = 0
+          for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -ref));
+        // O^T (HD x 32) += V_tile^T P^T ; l += sum of the lane's P
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+        for (int kt = 0; kt < BC / 16; ++kt) {
+          const vec8<T> pf = acc_to_frag<T>(s[kt >> 1], 8 * (kt & 1));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -ref));
-      // O^T (HD x 32) += V_tile^T P^T ; l += sum of the lane's P
-#pragma unroll
-      for (int kt = 0; kt < BC / 16; ++kt) {
-        const vec8<T> pf = acc_to_frag<T>(s[kt >> 1], 8 * (kt & 1));
-#pragma unroll
-        for (int d = 0; d < HD / 32; ++d) oacc[d] = mma<T>(Tile::tr_frag(Vs, kt, 32 * d, lane), pf, oacc[d]);
-        lsum = frag_sum(pf, lsum);
+          for (int d = 0; d < HD / 32; ++d) oacc[d] = mma<T>(Tile::tr_frag(Vs, kt, 32 * d, lane), pf, oacc[d]);
+          lsum = frag_sum(pf, lsum);
+        }
       }
     }
     if (more) {
@@ -195,9 +209,9 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     }
     __syncthreads();
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    tile(it, lds_a, lds_b);
-    if (it + 1 < ntiles) tile(it + 1, lds_b, lds_a);
+  for (int it = 0; it < nstages; it += 2) {
+    stage(it, lds_a, lds_b);
+    if (it + 1 < nstages) stage(it + 1, lds_b, lds_a);
   }
 
   const float l = wave_xor32_sum(lsum);
@@ -217,11 +231,13 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 
 template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW>
 static void launch_fwd_nw(const FwdArgs& a, hipStream_t st) {
-  constexpr int BC = 64, BR = 32 * NW;
+  // 8-wave workgroups (one per CU) load and synchronise per 128 keys, in two
+  // buffers of up to 64 KiB; 4-wave ones (two per CU) per 64 keys
+  constexpr int BC = 64, BS = (NW == 8 && sizeof(T) == 2) ? 128 : 64, BR = 32 * NW;
   const int nqt = (a.pb.Sq + BR - 1) / BR;
   dim3 grid(nqt * a.pb.B * a.pb.Hq), block(NW * 64);
   if (grid.x > 0)
-    hipLaunchKernelGGL((fwd_kernel<T, HD, BC, NW, CAUSAL, WINDOW>), grid, block, 0, st, (const T*)a.q,
+    hipLaunchKernelGGL((fwd_kernel<T, HD, BC, BS, NW, CAUSAL, WINDOW>), grid, block, 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.pb, a.scale * kLog2e, nqt);
 }
 

@@ -214,15 +214,22 @@ def test_equal_lengths_ex_matches_plain_bitwise():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("causal,window", [(False, None), (True, 300), (False, 700)])
-def test_wide_grid_masks(causal, window):
+WIDE = [(False, None, 2048, 2048, 128), (True, 300, 2048, 2048, 128), (False, 700, 2048, 2048, 128),
+        (True, None, 1999, 1999, 128), (False, None, 1999, 1999, 128), (True, None, 1800, 2113, 128),
+        (False, None, 2001, 1937, 128), (True, 450, 2040, 2040, 64)]
+
+
+@pytest.mark.parametrize("causal,window,S,Skv,D", WIDE)
+def test_wide_grid_masks(causal, window, S, Skv, D):
     """A grid large enough for the 8-wave workgroups of the forward and dQ kernels
-    (B=8, 32/8 heads, S=2048, D=128, bf16) with the non-causal and windowed masks:
-    sampled rows of every head against the oracle, and one whole KV group's gradients."""
-    B, Hq, Hkv, S, D, dtype = 8, 32, 8, 2048, 128, "bf16"
+    (B=8, 32/8 heads, bf16) with the causal, non-causal and windowed masks, key
+    counts that end inside a 128-key load stage and keys longer or shorter than the
+    queries: sampled rows of every head against the oracle, and one whole KV group's
+    gradients."""
+    B, Hq, Hkv, dtype = 8, 32, 8, "bf16"
     scale = 1.0 / math.sqrt(D)
-    inp = make_inputs(B, Hq, Hkv, S, D, dtype, seed=4200 + (window or 0), q_std=2.0)
-    what = f"wide grid causal={causal} window={window}"
+    inp = make_inputs(B, Hq, Hkv, S, D, dtype, seed=4200 + (window or 0) + S + Skv + D, q_std=2.0, Skv=Skv)
+    what = f"wide grid causal={causal} window={window} Sq={S} Skv={Skv} D={D}"
     say("case", what)
     o, lse, (dq, dk, dv) = run_dense(inp, dtype, scale, causal, window)
     rng = np.random.default_rng(9)
