@@ -281,10 +281,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
-  const int work = xcd_slice(blockIdx.x, gridDim.x);  // head-major, heaviest tile first
-  const int bh = work / nqt;
-  const int qt = CAUSAL ? (nqt - 1 - (work - bh * nqt)) : (work - bh * nqt);
-  const int b = bh / pb.Hq, hq = bh - b * pb.Hq;
+  const QTile wt = qtile_of<CAUSAL>(xcd_slice(blockIdx.x, gridDim.x), nqt, pb);
+  const int b = wt.b, hq = wt.hq, qt = wt.qt;
   const Seq sv = seq_of(pb, b, hq, hq / (pb.Hq / pb.Hkv));
   const int i0 = qt * BR;
   if (i0 >= sv.sq) return;

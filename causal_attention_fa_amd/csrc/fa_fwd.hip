@@ -33,8 +33,10 @@
 //     before them), and the element mask is applied on edge tiles only;
 //   * packed variable-length batches: a workgroup past its sequence's end
 //     returns at once; every sequence has its own key offset;
-//   * each XCD takes a contiguous run of heads, so the query heads of a KV
-//     group stream that group's K/V through one L2.
+//   * work items run KV group by KV group, and within a group query tile by
+//     query tile with the group's heads side by side; each XCD takes a
+//     contiguous run of them, so the heads that stream the same K/V rows do
+//     so at the same time through one L2.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -66,12 +68,10 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
-  // work item: (b*Hq + hq) major, query tiles heaviest first within a head;
-  // one XCD takes a contiguous run of heads (a KV group for GQA)
-  const int work = xcd_slice(blockIdx.x, gridDim.x);
-  const int bh = work / nqt;
-  const int qt = CAUSAL ? (nqt - 1 - (work - bh * nqt)) : (work - bh * nqt);
-  const int b = bh / pb.Hq, hq = bh - b * pb.Hq;
+  // work item: KV group major, then query tile (heaviest first), then the
+  // group's heads; one XCD takes a contiguous run of work items
+  const QTile wt = qtile_of<CAUSAL>(xcd_slice(blockIdx.x, gridDim.x), nqt, pb);
+  const int b = wt.b, hq = wt.hq, qt = wt.qt;
   const Seq sv = seq_of(pb, b, hq, hq / (pb.Hq / pb.Hkv));
   const int i0 = qt * BR;
   if (i0 >= sv.sq) return;  // a shorter sequence of a packed batch: no rows here

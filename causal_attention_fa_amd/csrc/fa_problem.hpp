@@ -54,6 +54,22 @@ __device__ inline Seq seq_of(const Problem& p, int b, int hq, int hkv) {
 // one sequence (the query layouts' head stride).
 __device__ inline size_t q_head_stride(const Problem& p) { return p.cu_q != nullptr ? (size_t)p.Tq : (size_t)p.Sq; }
 
+// Work item of a kernel over query tiles: KV group major, then query tile
+// (heaviest first when causal), then the group's query heads.  The G heads
+// that read the same K/V rows run side by side and share them in L2.
+struct QTile {
+  int b, hq, qt;
+};
+template <bool CAUSAL>
+__device__ inline QTile qtile_of(int work, int nqt, const Problem& p) {
+  const int G = p.Hq / p.Hkv;
+  const int rest = work / G;
+  const int t = rest % nqt;
+  const int bk = rest / nqt;
+  const int b = bk / p.Hkv;
+  return {b, (bk - b * p.Hkv) * G + (work - rest * G), CAUSAL ? nqt - 1 - t : t};
+}
+
 // Visibility of key j to query i (both relative to their sequence); the mask
 // kinds are compile-time so the common causal-only path carries no window.
 template <bool CAUSAL, bool WINDOW>
