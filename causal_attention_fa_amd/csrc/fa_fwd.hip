@@ -104,10 +104,15 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   const int jt0 = lo / BS;
   const int nstages = hi > lo ? (hi + BS - 1) / BS - jt0 : 0;
 
-  LoopLoader<T, BS, HD, NT> kld, vld;
+  // In 8-wave workgroups only waves 0-3 issue the K/V loads: a wave that
+  // issues loads waits until the memory pipeline has taken them, and the
+  // other wave of its SIMD keeps the matrix core busy meanwhile.
+  constexpr int NTL = NW == 8 ? NT / 2 : NT;
+  const bool loader = __builtin_amdgcn_readfirstlane(tid >> 6) < NTL / 64;
+  LoopLoader<T, BS, HD, NTL> kld, vld;
   kld.init(tid);
   vld.init(tid);
-  if (nstages > 0) {
+  if (nstages > 0 && loader) {
     kld.issue(Kh, jt0 * BS, sv.skv, lds_a, tid);
     vld.issue(Vh, jt0 * BS, sv.skv, lds_a + Stage::kElems, tid);
     kld.land(tid);
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   auto stage = [&](const int it, const T* cur, T* nxt) __attribute__((always_inline)) {
     const int s0 = (jt0 + it) * BS;
     const bool more = it + 1 < nstages;
-    if (more) {  // the other buffer was last read before the previous barrier
+    if (more && loader) {  // the other buffer was last read before the previous barrier
       kld.issue(Kh, s0 + BS, sv.skv, nxt, tid);
       vld.issue(Vh, s0 + BS, sv.skv, nxt + Stage::kElems, tid);
     }
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
         }
       }
     }
-    if (more) {
+    if (more && loader) {
       kld.land(tid);
       vld.land(tid);
     }
