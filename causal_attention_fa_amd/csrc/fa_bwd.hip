@@ -76,7 +76,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   using VTile = RowTile<T, BKV, HD>;
   __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
   __shared__ __attribute__((aligned(16))) T lds_v[VTile::kElems];  // this workgroup's V rows
-  __shared__ __attribute__((aligned(16))) float lds_ld[2][2][BQ];  // [buf][L*log2e, D][row]
+  __shared__ __attribute__((aligned(16))) float lds_ld[2][2][BQ];  // [buf][L*log2e, -D][row]
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     dold.land(tid);
     if (tid < BQ) {
       lds_ld[buf][0][tid] = ld_l * kLog2e;
-      lds_ld[buf][1][tid] = ld_d;
+      lds_ld[buf][1][tid] = -ld_d;
     }
   };
 
@@ -185,17 +185,24 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     const bool active = (!CAUSAL || i0 + BQ - 1 + off >= kw0) &&
                         (!WINDOW || i0 + off - pb.window <= kw0 + 31);
     if (active) {
-      // S, dP (BQ x 32): rows = queries of the tile, columns = this wave's keys
+      // S, dP - D (BQ x 32): rows = queries of the tile, columns = this wave's
+      // keys; the dP products start from -D of their rows, so dS = P (dP - D)
+      // needs one multiply per element
       f32x16 s[BQ / 32], dp[BQ / 32];
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {
-        s[qb] = f32x16{};
-        dp[qb] = f32x16{};
+        f32x16 nd;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&lds_ld[buf][1][32 * qb + 8 * g4 + 4 * h]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nd[4 * g4 + e] = x[e];
+        }
 #pragma unroll
         for (int t = 0; t < HD / 16; ++t) {
-          s[qb] = mma<T>(Tile::frag(Qs, 32 * qb + r, 16 * t, h), kf[t], s[qb]);
+          s[qb] = mma<T>(Tile::frag(Qs, 32 * qb + r, 16 * t, h), kf[t], t == 0 ? f32x16{} : s[qb]);
           dp[qb] = mma<T>(Tile::frag(dOs, 32 * qb + r, 16 * t, h), VTile::frag(lds_v, 32 * w + r, 16 * t, h),
-                          dp[qb]);
+                          t == 0 ? nd : dp[qb]);
         }
         if constexpr (sizeof(T) == 2) {
           // the Q, dO and V fragments of step t+1 are read before the products of step t
@@ -218,7 +225,6 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
         for (int g4 = 0; g4 < 4; ++g4) {
           const int qrow = 32 * qb + 8 * g4 + 4 * h;  // first of 4 consecutive query rows
           const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][0][qrow]);
-          const f32x4 dvv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][1][qrow]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * g4 + e;
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
               p = vis ? p : 0.f;
             }
             s[qb][i] = p;
-            dp[qb][i] = p * (dp[qb][i] - dvv[e]);
+            dp[qb][i] = p * dp[qb][i];
           }
         }
       // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over the tile's queries)
