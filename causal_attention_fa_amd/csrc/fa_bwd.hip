@@ -79,7 +79,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   __shared__ __attribute__((aligned(16))) float lds_ld[2][2][BQ];  // [buf][L*log2e, -D][row]
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
+  const int lane = tid & 63, r = lane & 31, h = lane >> 5;
   // work item: (b*Hkv + hkv) major, key tiles in order within a group (small
   // key tiles see the most queries: launched first); one XCD takes a
   // contiguous run, so the group's Q and dO stream through one L2
@@ -286,7 +287,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
+  const int lane = tid & 63, r = lane & 31, h = lane >> 5;
   const QTile wt = qtile_of<CAUSAL>(xcd_slice(blockIdx.x, gridDim.x), nqt, pb);
   const int b = wt.b, hq = wt.hq, qt = wt.qt;
   const Seq sv = seq_of(pb, b, hq, hq / (pb.Hq / pb.Hkv));
@@ -450,10 +452,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   mark(a.ev, a.nev, 2, st);
   // dQ: 8-wave workgroups when there are enough of them (as the forward)
-  if (sizeof(T) == 2 && (long long)((pb.Sq + 255) / 256) * pb.B * pb.Hq >= kWideGrid)
-    launch_dq_nw<T, HD, 8, CAUSAL, WINDOW>(a, st, c);
-  else
-    launch_dq_nw<T, HD, 4, CAUSAL, WINDOW>(a, st, c);
+  bool wide = false;
+  if constexpr (sizeof(T) == 2) {  // fp32 keeps 4-wave workgroups (no 8-wave instances)
+    wide = (long long)((pb.Sq + 255) / 256) * pb.B * pb.Hq >= kWideGrid;
+    if (wide) launch_dq_nw<T, HD, 8, CAUSAL, WINDOW>(a, st, c);
+  }
+  if (!wide) launch_dq_nw<T, HD, 4, CAUSAL, WINDOW>(a, st, c);
   mark(a.ev, a.nev, 3, st);
   return hipGetLastError();
 }

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(SplitCfg<T>::NW * 64, 1) void split_kernel(
   __shared__ __attribute__((aligned(16))) T lds[2 * kBuf];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
+  const int lane = tid & 63, r = lane & 31, h = lane >> 5;
   const int split = blockIdx.x % nsplit;
   const int bg = blockIdx.x / nsplit;
   const int b = bg / pb.Hkv, hkv = bg - b * pb.Hkv;

@@ -168,12 +168,18 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
         const bool edge = (CAUSAL && j0 + BC - 1 > qw0 + off) ||
                           (WINDOW && j0 < qw0 + 31 + off - pb.window) || (j0 + BC > sv.skv);
         if (edge) {
+          // key j0 + 4h + e (e a constant per register) is visible to row myq
+          // when e < e_end, e <= e_diag (causal) and e >= e_win (window): the
+          // rule of key_visible with the lane's terms taken out once
+          const int base = j0 + 4 * h;
+          const int e_end = sv.skv - base, e_diag = myq + off - base, e_win = myq + off - pb.window - base;
 #pragma unroll
           for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-              s[kb][i] = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? s[kb][i] : -INFINITY;
+              const int e = 32 * kb + 8 * (i >> 2) + (i & 3);
+              const bool vis = e < e_end && (!CAUSAL || e <= e_diag) && (!WINDOW || e >= e_win);
+              s[kb][i] = vis ? s[kb][i] : -INFINITY;
             }
         }
         float mx = -INFINITY;
@@ -252,10 +258,12 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   // 16-bit: workgroups of 8 waves (256 query rows) share each K/V tile among
   // twice the waves, which is faster when there are enough of them to fill
   // the GPU several times over (one such workgroup fits a CU at a time)
-  if (sizeof(T) == 2 && (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq >= kWideGrid)
-    launch_fwd_nw<T, HD, 8, CAUSAL, WINDOW>(a, st);
-  else
-    launch_fwd_nw<T, HD, 4, CAUSAL, WINDOW>(a, st);
+  bool wide = false;
+  if constexpr (sizeof(T) == 2) {  // fp32 keeps 4-wave workgroups (no 8-wave instances)
+    wide = (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq >= kWideGrid;
+    if (wide) launch_fwd_nw<T, HD, 8, CAUSAL, WINDOW>(a, st);
+  }
+  if (!wide) launch_fwd_nw<T, HD, 4, CAUSAL, WINDOW>(a, st);
   mark(a.ev, a.nev, 1, st);
   return hipGetLastError();
 }
