@@ -279,7 +279,10 @@ def forward_sweep(steps, warmup):
             if st != fa.FA_OK:
                 raise fa.FAError(st, "fa_fwd")
 
-        ms, _ = _time_calls(fwd, steps, warmup, sh, hip)
+        # short kernels: warm up and time for a fixed span (~0.1 s, ~0.2 s), so
+        # that the clock has settled and one launch's overhead does not count
+        est, _ = _time_calls(fwd, 3, 1, sh, hip)
+        ms, _ = _time_calls(fwd, max(steps, int(200 / est)), max(warmup, int(100 / est)), sh, hip)
         tf = 4.0 * D * B * Hq * S * (S + 1) / 2 / (ms * 1e-3) / 1e12
         out.append({"S": S, "ms": round(ms, 4), "tflops": round(tf, 1),
                     "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)})

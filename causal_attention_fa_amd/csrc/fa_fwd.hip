@@ -255,12 +255,13 @@ static void launch_fwd_nw(const FwdArgs& a, hipStream_t st) {
 template <typename T, int HD, bool CAUSAL, bool WINDOW>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   mark(a.ev, a.nev, 0, st);
-  // 16-bit: workgroups of 8 waves (256 query rows) share each K/V tile among
-  // twice the waves, which is faster when there are enough of them to fill
-  // the GPU several times over (one such workgroup fits a CU at a time)
+  // 16-bit: workgroups of 8 waves (256 query rows; one fits a CU at a time)
+  // share each K/V tile among twice the waves.  Measured: at D = 128 they are
+  // faster from one workgroup per CU up (S = 4096 to 16384, and B = 4 at
+  // S = 2048); at D = 64 only when they fill the GPU several times over.
   bool wide = false;
   if constexpr (sizeof(T) == 2) {  // fp32 keeps 4-wave workgroups (no 8-wave instances)
-    wide = (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq >= kWideGrid;
+    wide = (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq >= (HD == 128 ? kCUs : kWideGrid);
     if (wide) launch_fwd_nw<T, HD, 8, CAUSAL, WINDOW>(a, st);
   }
   if (!wide) launch_fwd_nw<T, HD, 4, CAUSAL, WINDOW>(a, st);

@@ -22,9 +22,12 @@ struct FwdArgs {
   int nev;
 };
 
-// Grids of at least this many 8-wave workgroups (8 per CU) run the forward
-// and dQ kernels with 8 waves per workgroup; smaller ones use 4.
+// Grids of at least this many 8-wave workgroups (8 per CU) run the dQ
+// kernel (and the forward at D = 64) with 8 waves per workgroup; smaller ones
+// use 4.
 constexpr long long kWideGrid = 2048;
+// compute units of an MI355X
+constexpr long long kCUs = 256;
 
 // Records ev[i] on the stream when instrumentation asked for it.
 inline void mark(hipEvent_t* ev, int nev, int i, hipStream_t st) {
