@@ -257,11 +257,13 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   mark(a.ev, a.nev, 0, st);
   // 16-bit: workgroups of 8 waves (256 query rows; one fits a CU at a time)
   // share each K/V tile among twice the waves.  Measured: at D = 128 they are
-  // faster from one workgroup per CU up (S = 4096 to 16384, and B = 4 at
-  // S = 2048); at D = 64 only when they fill the GPU several times over.
+  // faster from one workgroup per CU up when the queries fill their rows
+  // (S = 4096 to 16384, and B = 4 at S = 2048); otherwise (D = 64, short
+  // query blocks) only when they fill the GPU several times over.
   bool wide = false;
   if constexpr (sizeof(T) == 2) {  // fp32 keeps 4-wave workgroups (no 8-wave instances)
-    wide = (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq >= (HD == 128 ? kCUs : kWideGrid);
+    const long long n8 = (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq;
+    wide = n8 >= ((HD == 128 && a.pb.Sq >= 256) ? kCUs : kWideGrid);
     if (wide) launch_fwd_nw<T, HD, 8, CAUSAL, WINDOW>(a, st);
   }
   if (!wide) launch_fwd_nw<T, HD, 4, CAUSAL, WINDOW>(a, st);
