@@ -36,6 +36,8 @@
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
+#include <type_traits>
+
 namespace fa {
 
 // ------------------------------------------------------------------ D = rowsum(dO * O)
@@ -220,26 +222,57 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
       // past the end only feed dK / dV columns that are never stored)
       const bool edge = (CAUSAL && i0 + off < kw0 + 31) ||
                         (WINDOW && i0 + BQ - 1 + off - pb.window > kw0) || (i0 + BQ > sv0.sq);
+      if constexpr (CAUSAL && !WINDOW) {
+        // masked pairs get P = dS = 0 in a branch of their own: with the mask
+        // inside the loop the compiler computed it (and selected) every tile
 #pragma unroll
-      for (int qb = 0; qb < BQ / 32; ++qb)
+        for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int qrow = 32 * qb + 8 * g4 + 4 * h;  // first of 4 consecutive query rows
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][0][qrow]);
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int qrow = 32 * qb + 8 * g4 + 4 * h;  // first of 4 consecutive query rows
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][0][qrow]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * g4 + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c, -lv[e]));
-            if (edge) {
-              const int q = i0 + qrow + e;
-              const bool vis = q < sv0.sq && (!CAUSAL || mykv <= q + off) &&
-                               (!WINDOW || mykv >= q + off - pb.window);
-              p = vis ? p : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * g4 + e;
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c, -lv[e]));
+              s[qb][i] = p;
+              dp[qb][i] = p * dp[qb][i];
             }
-            s[qb][i] = p;
-            dp[qb][i] = p * dp[qb][i];
           }
+        if (edge) {
+#pragma unroll
+          for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int q = i0 + 32 * qb + 8 * (i >> 2) + 4 * h + (i & 3);
+              const bool vis = q < sv0.sq && mykv <= q + off;
+              s[qb][i] = vis ? s[qb][i] : 0.f;
+              dp[qb][i] = vis ? dp[qb][i] : 0.f;
+            }
         }
+      } else {
+        // (the split form above needs more registers with these masks)
+#pragma unroll
+        for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int qrow = 32 * qb + 8 * g4 + 4 * h;
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][0][qrow]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * g4 + e;
+              float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c, -lv[e]));
+              if (edge) {
+                const int q = i0 + qrow + e;
+                const bool vis = q < sv0.sq && (!CAUSAL || mykv <= q + off) &&
+                                 (!WINDOW || mykv >= q + off - pb.window);
+                p = vis ? p : 0.f;
+              }
+              s[qb][i] = p;
+              dp[qb][i] = p * dp[qb][i];
+            }
+          }
+      }
       // dV^T += dO^T P ; dK^T += Q^T dS   (contraction over the tile's queries)
 #pragma unroll
       for (int kt = 0; kt < BQ / 16; ++kt) {
@@ -373,15 +406,23 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
+        // P and dS; the masked form is a branch of its own (a mask inside the
+        // loop is computed, and selected, for every tile)
+        auto elementwise = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lq));
-          if (edge) {
-            const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            p = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? p : 0.f;
+          for (int i = 0; i < 16; ++i) {
+            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lq));
+            if constexpr (decltype(masked)::value) {
+              const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+              p = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? p : 0.f;
+            }
+            dp[i] = p * (dp[i] - dq_d);
           }
-          dp[i] = p * (dp[i] - dq_d);
-        }
+        };
+        if (edge)
+          elementwise(std::true_type{});
+        else
+          elementwise(std::false_type{});
         // dQ^T (HD x 32) += K_block^T dS^T
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
