@@ -345,7 +345,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     }
   }
   const float lq = LSE[qrow] * kLog2e;
-  const float dq_d = Dd[qrow];
+  f32x16 ndq;  // -D of the lane's row in every slot: the start of its dP^T products
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndq[i] = -Dd[qrow];
   f32x16 acc[HD / 32];
 #pragma unroll
   for (int d = 0; d < HD / 32; ++d) acc[d] = f32x16{};
@@ -371,16 +373,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   // they would also wait for the loop's own assembly loads.
   __builtin_amdgcn_s_waitcnt(0);
 
-  for (int it = 0; it < ntiles; ++it) {
+  // unrolled by two: every LDS address names its buffer at compile time
+  auto tile = [&](const int it, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     const int j0 = (jt0 + it) * BC;
     const bool more = it + 1 < ntiles;
     if (more) {  // the other buffer was last read before the previous barrier
-      T* nb = lds + ((it + 1) & 1) * kElems;
+      T* nb = lds + (buf ^ 1) * kElems;
       kld.issue(Kh, j0 + BC, sv.skv, nb + kOffK, tid);
       vld.issue(Vh, j0 + BC, sv.skv, nb + kOffV, tid);
     }
-    const T* Ks = lds + (it & 1) * kElems + kOffK;
-    const T* Vs = lds + (it & 1) * kElems + kOffV;
+    const T* Ks = lds + buf * kElems + kOffK;
+    const T* Vs = lds + buf * kElems + kOffV;
     const bool active = (!CAUSAL || j0 <= qw0 + 31 + off) &&
                         (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
     if (active) {
@@ -390,11 +394,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
       // next block's are formed, which halves the accumulator registers
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        // dP^T starts from -D of the lane's row, so dS = P (dP - D) is one
+        // multiply per element
+        f32x16 s, dp;
 #pragma unroll
         for (int t = 0; t < HD / 16; ++t) {
-          s = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], s);
-          dp = mma<T>(Tile::frag(Vs, 32 * kb + r, 16 * t, h), df[t], dp);
+          s = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], t == 0 ? f32x16{} : s);
+          dp = mma<T>(Tile::frag(Vs, 32 * kb + r, 16 * t, h), df[t], t == 0 ? ndq : dp);
         }
         if constexpr (sizeof(T) == 2) {
           // the K and V fragments of step t+1 are read before the products of step t
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
               const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
               p = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? p : 0.f;
             }
-            dp[i] = p * (dp[i] - dq_d);
+            dp[i] = p * dp[i];
           }
         };
         if (edge)
@@ -439,6 +445,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
       vld.land(tid);
     }
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    tile(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) tile(it + 1, std::integral_constant<int, 1>{});
   }
 
   if (myq < sv.sq) {
