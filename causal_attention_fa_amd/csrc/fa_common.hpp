@@ -394,7 +394,9 @@ struct AsmTileLoader : TileLoader<T, ROWS, HD, NT, true> {
   static constexpr int kNW = Base::kNW, kInstr = Base::kInstr, kRowBytes = Base::kRowBytes;
   static constexpr int kRowsPerInstr = Base::kRowsPerInstr;
 
-  // LDS byte address of this wave's 1 KiB slice of instruction p (uniform)
+  // LDS byte address of this wave's 1 KiB slice of instruction p (uniform),
+  // handed to each load in M0 through the "{m0}" operand, so the compiler
+  // itself sets M0 and knows its value
   __device__ static inline uint32_t slice(T* lds, int p, int w) {
     const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)lds);
     return __builtin_amdgcn_readfirstlane(base + (uint32_t)((p * kNW + w) * 1024));
@@ -406,20 +408,20 @@ struct AsmTileLoader : TileLoader<T, ROWS, HD, NT, true> {
 #pragma unroll
       for (int p = 0; p < kInstr; ++p) {
         const char* src = gb + (size_t)p * kRowsPerInstr * kRowBytes;
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                      :
-                     : "s"(slice(lds, p, wslot)), "v"(off), "s"(src)
-                     : "memory", "m0");
+                     : "v"(off), "s"(src), "{m0}"(slice(lds, p, wslot))
+                     : "memory");
       }
     } else {
 #pragma unroll
       for (int p = 0; p < kInstr; ++p) {
         const int r = min(row0 + row + p * kRowsPerInstr, nvalid - 1);
         const char* src = reinterpret_cast<const char*>(g) + (size_t)r * kRowBytes + col;
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                      :
-                     : "s"(slice(lds, p, wslot)), "v"(src)
-                     : "memory", "m0");
+                     : "v"(src), "{m0}"(slice(lds, p, wslot))
+                     : "memory");
       }
     }
   }
