@@ -23,7 +23,9 @@
 //     the current stage's math; V^T fragments come from gfx950's LDS
 //     transpose read.  A stage is 128 keys (two 64-key tiles) for 8-wave
 //     workgroups, which have the CU's LDS to themselves, and one tile
-//     otherwise; the waves synchronise once per stage;
+//     otherwise; the waves synchronise once per stage, and in 8-wave
+//     workgroups only waves 0-3 issue the loads (the other wave of each SIMD
+//     keeps computing while a loading wave waits for the memory pipeline);
 //   * softmax in base 2: p = exp2(s * scale*log2e - m), m tracked in that unit,
 //     and the accumulator is rescaled only when a row's max grows by > 2^4;
 //   * the row sum l is taken over exactly the rounded P that multiplies V
