@@ -245,10 +245,13 @@ __device__ inline vec4<T> lds_tr4(const T* p) {
 template <typename T, int ROWS, int HD>
 __device__ inline vec8<T> RowTile<T, ROWS, HD>::tr_frag(const T* base, int kt, int col0, int lane) {
   if constexpr (sizeof(T) == 2) {
-    const int row = 16 * kt + 4 * (lane >> 5) + ((lane & 15) >> 2);
+    // the swizzle reads row bits 0..3 only: the lane's place within a group of
+    // 16 rows is the same for every kt, which then is a constant offset
+    const int x = 4 * (lane >> 5) + ((lane & 15) >> 2);
     const int col = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    vec4<T> a = lds_tr4<T>(base + at(row, col));
-    vec4<T> b = lds_tr4<T>(base + at(row + 8, col));
+    const T* g = base + 16 * kt * kStride;
+    vec4<T> a = lds_tr4<T>(g + at(x, col));
+    vec4<T> b = lds_tr4<T>(g + at(x + 8, col));
     return vec8<T>{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   } else {
     // fp32: eight scalar reads (only the small fp32 workloads take this path)

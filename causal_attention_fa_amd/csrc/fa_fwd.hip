@@ -21,8 +21,8 @@
 //   * K and V tiles are staged row-major (XOR-swizzled) in LDS, double
 //     buffered: the next stage's direct global->LDS loads are issued before
 //     the current stage's math; V^T fragments come from gfx950's LDS
-//     transpose read.  A stage is 128 keys (two 64-key tiles) for 8-wave
-//     workgroups, which have the CU's LDS to themselves, and one tile
+//     transpose read.  A stage (and tile) is 128 keys for 8-wave
+//     workgroups, which have the CU's LDS to themselves, and 64 keys
 //     otherwise; the waves synchronise once per stage, and in 8-wave
 //     workgroups only waves 0-3 issue the loads (the other wave of each SIMD
 //     keeps computing while a loading wave waits for the memory pipeline);
@@ -62,11 +62,11 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   using Stage = RowTile<T, BS, HD>;  // the unit of the loads and barriers: BS keys
   constexpr int kSub = BS / BC;
   static_assert(BS % BC == 0 && BC % 16 == 0, "a stage is whole tiles; the swizzle repeats every 16 rows");
-  constexpr int kBuf = 2 * Stage::kElems;  // K stage, then V stage
-  // Two buffers as two LDS variables, and the stage loop unrolled by two, so
-  // that every LDS address is a register plus a constant offset.
-  __shared__ __attribute__((aligned(16))) T lds_a[kBuf];
-  __shared__ __attribute__((aligned(16))) T lds_b[kBuf];
+  // Two buffers laid out as K stage 0, K stage 1, V stage 0, V stage 1, and
+  // the stage loop unrolled by two: a lane's K (or V) fragments of either
+  // buffer are one register each plus a constant offset below 64 KiB.
+  constexpr int kVOff = 2 * Stage::kElems;
+  __shared__ __attribute__((aligned(16))) T lds[2 * kVOff];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
@@ -115,8 +115,8 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   kld.init(tid);
   vld.init(tid);
   if (nstages > 0 && loader) {
-    kld.issue(Kh, jt0 * BS, sv.skv, lds_a, tid);
-    vld.issue(Vh, jt0 * BS, sv.skv, lds_a + Stage::kElems, tid);
+    kld.issue(Kh, jt0 * BS, sv.skv, lds, tid);
+    vld.issue(Vh, jt0 * BS, sv.skv, lds + kVOff, tid);
     kld.land(tid);
     vld.land(tid);
   }
@@ -126,7 +126,13 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   // they would also wait for the loop's own assembly loads.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // one KV stage: compute on `cur` while the next stage streams into `nxt`.
+  // The V stages' offset, opaque to the compiler: it then forms each lane's V
+  // addresses once and reaches every V tile by a constant offset (a constant
+  // of 64 KiB or more it folds into every address instead).
+  int voff = kVOff;
+  asm("" : "+s"(voff));
+  // one KV stage: compute on `cur` while the next stage streams into `nxt`
+  // (the K stages; each V stage sits kVOff further on).
   // The waves synchronise once per stage; within it each wave runs through
   // the stage's tiles at its own pace.
   auto stage = [&](const int it, const T* cur, T* nxt) __attribute__((always_inline)) {
@@ -134,13 +140,13 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     const bool more = it + 1 < nstages;
     if (more && loader) {  // the other buffer was last read before the previous barrier
       kld.issue(Kh, s0 + BS, sv.skv, nxt, tid);
-      vld.issue(Vh, s0 + BS, sv.skv, nxt + Stage::kElems, tid);
+      vld.issue(Vh, s0 + BS, sv.skv, nxt + kVOff, tid);
     }
 #pragma unroll
     for (int sub = 0; sub < kSub; ++sub) {
       const int j0 = s0 + sub * BC;
       const T* Ks = cur + sub * Tile::kElems;
-      const T* Vs = cur + Stage::kElems + sub * Tile::kElems;
+      const T* Vs = cur + voff + sub * Tile::kElems;
       // does any of this wave's rows see a key of the tile?
       const bool active = j0 < hi && (!CAUSAL || j0 <= qw0 + 31 + off) &&
                           (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
@@ -223,8 +229,8 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     __syncthreads();
   };
   for (int it = 0; it < nstages; it += 2) {
-    stage(it, lds_a, lds_b);
-    if (it + 1 < nstages) stage(it + 1, lds_b, lds_a);
+    stage(it, lds, lds + Stage::kElems);
+    if (it + 1 < nstages) stage(it + 1, lds + Stage::kElems, lds);
   }
 
   const float l = wave_xor32_sum(lsum);
@@ -244,9 +250,10 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 
 template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW>
 static void launch_fwd_nw(const FwdArgs& a, hipStream_t st) {
-  // 8-wave workgroups (one per CU) load and synchronise per 128 keys, in two
-  // buffers of up to 64 KiB; 4-wave ones (two per CU) per 64 keys
-  constexpr int BC = 64, BS = (NW == 8 && sizeof(T) == 2) ? 128 : 64, BR = 32 * NW;
+  // 8-wave workgroups (one per CU) load, synchronise and compute per 128 keys,
+  // in two buffers of up to 64 KiB; 4-wave ones (two per CU) per 64 keys.  A
+  // 128-key tile takes one row max, exchange and rescale test per 128 keys.
+  constexpr int BS = (NW == 8 && sizeof(T) == 2) ? 128 : 64, BC = BS, BR = 32 * NW;
   const int nqt = (a.pb.Sq + BR - 1) / BR;
   dim3 grid(nqt * a.pb.B * a.pb.Hq), block(NW * 64);
   if (grid.x > 0)

@@ -155,10 +155,14 @@ def test_varlen(case):
     compare(run_varlen(inp, dtype, scale, causal, window, Hq), ref, dtype, what)
 
 
-def test_varlen_matches_dense_calls_bitwise():
+def test_varlen_matches_dense_calls():
     """At full size (16401 packed tokens, 32 query / 8 KV heads, D = 128, bf16): every
-    sequence of the packed call equals a dense call on that sequence alone, bit for
-    bit (same kernels, same per-tile arithmetic), and sampled rows meet the oracle."""
+    sequence of the packed call matches a dense call on that sequence alone.  Where the
+    dense call runs the same kernels (8-wave forward tiles of 128 keys: 2048 tokens or
+    more at 32 heads) the two agree bit for bit, which also rules out a single key
+    leaking across a sequence boundary; shorter sequences run the 4-wave forward, whose
+    64-key tiles round differently, and meet the oracle's bounds against it.  Sampled
+    rows of long and short sequences meet the oracle."""
     lens = (8192, 4096, 2048, 1024, 512, 256, 128, 64, 64, 17)
     Hq, Hkv, D, dtype = 32, 8, 128, "bf16"
     scale = 1.0 / math.sqrt(D)
@@ -166,17 +170,21 @@ def test_varlen_matches_dense_calls_bitwise():
     say("case varlen full size", lens)
     o, lse, (dq, dk, dv) = run_varlen(inp, dtype, scale, True, None, Hq)
     cu = inp["cu_q"]
-    for b in (0, 4, 9):
+    for b in (0, 2, 4, 9):
         r0, r1 = int(cu[b]), int(cu[b + 1])
         sub = {n: np.ascontiguousarray(inp[n][None, :, r0:r1]) for n in ("q", "k", "v", "do")}
         do_, dl, (dq_, dk_, dv_) = run_dense(sub, dtype, scale, True, None)
-        for name, a, ref in (("o", o[:, r0:r1], do_[0]), ("lse", lse[:, r0:r1], dl[0]),
-                             ("dq", dq[:, r0:r1], dq_[0]), ("dk", dk[:, r0:r1], dk_[0]),
-                             ("dv", dv[:, r0:r1], dv_[0])):
-            assert np.array_equal(a, ref), f"sequence {b} {name} differs from the dense call"
+        got = (o[:, r0:r1], lse[:, r0:r1], (dq[:, r0:r1], dk[:, r0:r1], dv[:, r0:r1]))
+        if lens[b] >= 2048:
+            for name, a, ref in (("o", got[0], do_[0]), ("lse", got[1], dl[0]), ("dq", got[2][0], dq_[0]),
+                                 ("dk", got[2][1], dk_[0]), ("dv", got[2][2], dv_[0])):
+                assert np.array_equal(a, ref), f"sequence {b} {name} differs from the dense call"
+        else:
+            compare(got, {"o": do_[0], "lse": dl[0], "dq": dq_[0], "dk": dk_[0], "dv": dv_[0]}, dtype,
+                    f"sequence {b} against its dense call")
     rng = np.random.default_rng(5)
     dq_got, dq_ref = [], []
-    for b in (0, 2, 9):
+    for b in (0, 2, 4, 9):
         r0, n = int(cu[b]), lens[b]
         rows = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 6)]))
         for h in (0, 13, 31):
