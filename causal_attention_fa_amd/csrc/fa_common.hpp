@@ -399,7 +399,15 @@ struct AsmTileLoader : TileLoader<T, ROWS, HD, NT, true> {
 
   // LDS byte address of this wave's 1 KiB slice of instruction p (uniform),
   // handed to each load in M0 through the "{m0}" operand, so the compiler
-  // itself sets M0 and knows its value
+  // itself sets M0 and knows its value.
+  //
+  // Each load starts with 5 wait states (s_nop 4).  A vector memory
+  // instruction that reads an SGPR written by a VALU instruction (the
+  // compiler reloads spilled scalars with v_readlane) needs 5 of them, and
+  // one that reads M0 after a scalar write of it needs 1.  The compiler
+  // inserts these for its own memory instructions but cannot see that the
+  // assembly is one, so the assembly provides them itself; without them the
+  // load can take a stale base address.
   __device__ static inline uint32_t slice(T* lds, int p, int w) {
     const uint32_t base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) T*)lds);
     return __builtin_amdgcn_readfirstlane(base + (uint32_t)((p * kNW + w) * 1024));
@@ -411,7 +419,7 @@ struct AsmTileLoader : TileLoader<T, ROWS, HD, NT, true> {
 #pragma unroll
       for (int p = 0; p < kInstr; ++p) {
         const char* src = gb + (size_t)p * kRowsPerInstr * kRowBytes;
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                      :
                      : "v"(off), "s"(src), "{m0}"(slice(lds, p, wslot))
                      : "memory");
@@ -421,7 +429,7 @@ struct AsmTileLoader : TileLoader<T, ROWS, HD, NT, true> {
       for (int p = 0; p < kInstr; ++p) {
         const int r = min(row0 + row + p * kRowsPerInstr, nvalid - 1);
         const char* src = reinterpret_cast<const char*>(g) + (size_t)r * kRowBytes + col;
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
                      :
                      : "v"(src), "{m0}"(slice(lds, p, wslot))
                      : "memory");
