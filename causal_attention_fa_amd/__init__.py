@@ -12,6 +12,8 @@ optional sliding window) and ``forward_varlen`` / ``backward_varlen`` (packed
 variable-length batches) are conveniences for PyTorch callers: they allocate
 the outputs (and the backward workspace) with torch on the inputs' device, pass
 torch's current stream, and raise ``FAError`` on a non-OK status.
+``attention`` wraps ``forward`` and ``backward`` as one differentiable torch
+operation: its autograd node keeps the forward's O and L for the backward.
 
 There is no fallback: if libfa.so has not been built, loading raises.
 """
@@ -27,7 +29,7 @@ __all__ = [
     "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_profile_events",
     "fa_params_t", "params", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes",
     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
-    "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv",
+    "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv", "attention",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
@@ -318,3 +320,36 @@ def forward_splitkv(q, k, v, scale=None, causal=True, window=None, num_splits=0,
     if st != FA_OK:
         raise FAError(st, "fa_fwd_splitkv")
     return o, lse
+
+
+_attention_fn = None
+
+
+def attention(q, k, v, scale=None, causal=True, window=None):
+    """o for device tensors q [B,Hq,Sq,D], k, v [B,Hkv,Skv,D], differentiable in q, k and v.
+
+    The forward runs ``forward`` and keeps its outputs o and L (the logsumexp, the only
+    state the backward needs); the backward runs ``backward`` on them with the incoming
+    dO.  Both passes are the library's kernels; this only connects them to autograd."""
+    global _attention_fn
+    if _attention_fn is None:
+        torch = _torch()
+
+        class _Attention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, scale, causal, window):
+                o, lse = forward(q, k, v, scale=scale, causal=causal, window=window)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.cfg = (scale, causal, window)
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                scale, causal, window = ctx.cfg
+                dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), scale=scale, causal=causal,
+                                      window=window)
+                return dq, dk, dv, None, None, None
+
+        _attention_fn = _Attention
+    return _attention_fn.apply(q, k, v, scale, causal, window)
