@@ -100,20 +100,23 @@ DENSE_MUTANTS = [
 ]
 
 TILED_MUTANTS = [
-    ("ell = ell * alpha + p.sum(axis=1)", "ell = ell + p.sum(axis=1)"),
-    ("acc = acc * alpha[:, None] + p @ Vh[j0:j1]", "acc = acc + p @ Vh[j0:j1]"),
-    ("if causal and j0 > i1 - 1 + off:", "if causal and j0 > i0 + off:"),
-    ("bad = bad | (k_pos[None, :] < q_pos[:, None] + off - window)", "bad = bad | (k_pos[None, :] <= q_pos[:, None] + off - window)"),
-    ("last = Sq if window is None else min(Sq, j1 - 1 - off + window + 1)", "last = Sq if window is None else min(Sq, j1 - 1 - off + window)"),
-    ("m + np.log(np.where(seen, ell, 1.0))", "np.log(np.where(seen, ell, 1.0))"),
-    ("bad = bad | (k_pos[None, :] > q_pos[:, None] + off)", "bad = bad | (k_pos[None, :] >= q_pos[:, None] + off)"),
-    ("np.exp(s - lse[b, h, i0:i1, None])", "np.exp(s - 0 * lse[b, h, i0:i1, None])"),
-    ("ds = p * (dp - Dvec[b, h, i0:i1, None])", "ds = p * (dp + Dvec[b, h, i0:i1, None])"),
-    ("dQ[b, h, i0:i1] += scale * (ds @ Kj)", "dQ[b, h, i0:i1] += scale * (p @ Kj)"),
-    ("dKj += scale * (ds.T @ Qi)", "dKj += (ds.T @ Qi)"),
+    ("self.l *= alpha", "self.l *= 1.0"),                                   # l not rescaled
+    ("self.acc *= alpha[:, None]", "self.acc *= 1.0"),                      # acc not rescaled
+    ("hi = min(Skv, i1 + off) if causal else Skv", "hi = min(Skv, i0 + off + 1) if causal else Skv"),
+    ("vis &= kk >= qq + off - window", "vis &= kk > qq + off - window"),
+    ("stop = Sq if window is None else min(Sq, j1 - 1 - off + window + 1)",
+     "stop = Sq if window is None else min(Sq, j1 - 1 - off + window)"),
+    ("lse[seen] = self.m[seen] + np.log(self.l[seen])", "lse[seen] = np.log(self.l[seen])"),
+    ("vis &= kk <= qq + off", "vis &= kk < qq + off"),
+    ("p[vis] = np.exp((s - lse[b, h, i0:i1, None])[vis])", "p[vis] = np.exp(s[vis])"),
+    ("ds = p * (dp - rowdot[b, h, i0:i1, None])", "ds = p * (dp + rowdot[b, h, i0:i1, None])"),
+    ("dQ[b, h, i0:i1] += scale * (ds @ Kt)", "dQ[b, h, i0:i1] += scale * (p @ Kt)"),
+    ("gK += scale * (ds.T @ Qblk)", "gK += (ds.T @ Qblk)"),
     ("first = (max(0, j0 - off) // br) * br if causal else 0", "first = (j0 // br + 1) * br if causal else 0"),
-    ("Dvec = (do * o).sum(axis=-1)", "Dvec = (do * o).sum(axis=-1) * 0"),
-    ("g = h // G\n            Kh, Vh", "g = h % Hkv\n            Kh, Vh"),
+    ('rowdot = np.einsum("bhsd,bhsd->bhs", do, o)', 'rowdot = 0 * np.einsum("bhsd,bhsd->bhs", do, o)'),
+    ("kv = h // G\n            Kh, Vh", "kv = h % Hkv\n            Kh, Vh"),
+    ("weight[vis] = np.exp((logits - self.m[:, None])[vis])", "weight[vis] = np.exp(logits[vis])"),
+    ("gV += p.T @ dOblk", "gV += p.T @ dOblk * 0.5"),
 ]
 
 
