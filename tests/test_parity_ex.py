@@ -227,17 +227,20 @@ WIDE = [(False, None, 2048, 2048, 128), (True, 300, 2048, 2048, 128), (False, 70
         (False, None, 2001, 1937, 128), (True, 450, 2040, 2040, 64)]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal,window,S,Skv,D", WIDE)
-def test_wide_grid_masks(causal, window, S, Skv, D):
+def test_wide_grid_masks(causal, window, S, Skv, D, dtype):
     """A grid large enough for the 8-wave workgroups of the forward and dQ kernels
-    (B=8, 32/8 heads, bf16) with the causal, non-causal and windowed masks, key
-    counts that end inside a 128-key load stage and keys longer or shorter than the
-    queries: sampled rows of every head against the oracle, and one whole KV group's
-    gradients."""
-    B, Hq, Hkv, dtype = 8, 32, 8, "bf16"
+    (B=8, 32/8 heads: ceil(Sq/256) * 8 * 32 = 2048 eight-wave query blocks, which
+    dispatches the 8-wave forward at D = 128 from 256 and at D = 64 from 2048, and
+    the 8-wave dQ from 2048), in bf16 and fp16, with the causal, non-causal and
+    windowed masks, key counts that end inside a 128-key load stage and keys longer
+    or shorter than the queries: sampled rows of every head against the oracle, and
+    one whole KV group's gradients."""
+    B, Hq, Hkv = 8, 32, 8
     scale = 1.0 / math.sqrt(D)
     inp = make_inputs(B, Hq, Hkv, S, D, dtype, seed=4200 + (window or 0) + S + Skv + D, q_std=2.0, Skv=Skv)
-    what = f"wide grid causal={causal} window={window} Sq={S} Skv={Skv} D={D}"
+    what = f"wide grid {dtype} causal={causal} window={window} Sq={S} Skv={Skv} D={D}"
     say("case", what)
     o, lse, (dq, dk, dv) = run_dense(inp, dtype, scale, causal, window)
     rng = np.random.default_rng(9)
