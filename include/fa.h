@@ -30,13 +30,20 @@
  * written in the input dtype.
  *
  * Ownership and threading: every pointer is a device pointer owned by the
- * caller; the library allocates nothing and keeps no state between calls.
+ * caller; the library allocates nothing.  Its only state is the per-thread
+ * instrumentation pointer set by fa_profile_events (off unless a caller sets
+ * it; see there).
  * All work is enqueued on `stream` and the call returns without waiting.
  * Outputs are overwritten, never accumulated into.  Calls on different
  * streams with disjoint outputs may run concurrently.
  *
  * Errors: arguments are checked on the host before anything is enqueued; on
- * any error nothing is launched and no output is touched.
+ * any error nothing is launched and no output is touched.  An unsupported
+ * case is reported, never served by a slower substitute: the udemi.tech
+ * "Flash Attention" page forces the flash backend so that an impossible call
+ * raises instead of falling back, and "FlashAttention 与 SDPA Backend"
+ * (section 失败场景与生产实现差距) warns that an API accepting an argument
+ * does not mean every fast path supports it.
  *   FA_ERR_INVALID_ARG   null required pointer; B, Hq, Hkv, S or D < 0;
  *                        B, Hq or Hkv == 0 while there are query or key
  *                        rows; Hq % Hkv != 0; scale not finite; a pointer
@@ -85,7 +92,10 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * Bytes of device workspace fa_bwd needs for this problem (a multiple of 256;
- * 0 for an empty problem).  It holds the fp32 row dot products D[i].
+ * 0 for an empty problem).  It holds the fp32 row dot products
+ * D[i] = sum_d dO[i,d] * O[i,d], one per query row: the O(N) precompute of
+ * "Phase T14", decision ③, which the backward reads in place of the softmax
+ * Jacobian.  The library never allocates, so the caller provides it.
  * Returns 0 for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D);
@@ -109,7 +119,10 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    int B, int Hq, int Hkv, int S, int D, float scale, int causal,
                    fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Static, human-readable name of a status code ("FA_OK", ...); never NULL. */
+/* Static, human-readable name of a status code ("FA_OK", ...); never NULL.
+ * The codes follow the error convention above (an impossible request is an
+ * error, not a fallback: udemi.tech "Flash Attention", forcing the flash
+ * backend; "FlashAttention 与 SDPA Backend", section 失败场景与生产实现差距). */
 const char* fa_status_string(fa_status_t s);
 
 /*
@@ -209,8 +222,11 @@ fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
  * kernel, ev[2] before the dQ kernel and ev[3] after it; fa_fwd_splitkv
  * records ev[0] before its split kernel, ev[1] before its merge kernel and
  * ev[2] after it (fa_fwd_ex / fa_bwd_ex as fa_fwd / fa_bwd).  Indices >= n are not
- * recorded.  The caller owns the events (created with hipEventCreate) and must
- * keep them alive while in use; fa_profile_events(NULL, 0) turns recording off.
+ * recorded.  The caller owns the events (created with hipEventCreate).  The
+ * setting is state of the calling thread that lasts until changed: every later
+ * compute call on that thread records into the same events.  A caller must
+ * therefore call fa_profile_events(NULL, 0), which turns recording off, before
+ * it destroys the events; otherwise later calls record freed events.
  */
 void fa_profile_events(hipEvent_t* events, int n);
 
