@@ -161,8 +161,8 @@ def test_varlen_matches_dense_calls():
     dense call runs the same kernels (8-wave forward tiles of 128 keys: 2048 tokens or
     more at 32 heads) the two agree bit for bit, which also rules out a single key
     leaking across a sequence boundary; shorter sequences run the 4-wave forward, whose
-    64-key tiles round differently, and meet the oracle's bounds against it.  Sampled
-    rows of long and short sequences meet the oracle."""
+    64-key tiles round differently; there both calls meet the oracle's bounds.  Sampled
+    rows of long and short sequences meet the oracle, and so do whole short sequences."""
     lens = (8192, 4096, 2048, 1024, 512, 256, 128, 64, 64, 17)
     Hq, Hkv, D, dtype = 32, 8, 128, "bf16"
     scale = 1.0 / math.sqrt(D)
@@ -180,8 +180,12 @@ def test_varlen_matches_dense_calls():
                                  ("dk", got[2][1], dk_[0]), ("dv", got[2][2], dv_[0])):
                 assert np.array_equal(a, ref), f"sequence {b} {name} differs from the dense call"
         else:
-            compare(got, {"o": do_[0], "lse": dl[0], "dq": dq_[0], "dk": dk_[0], "dv": dv_[0]}, dtype,
-                    f"sequence {b} against its dense call")
+            # the dense call takes other kernels here, so both are held to the oracle
+            ref = oracle.sdpa_backward(sub["q"], sub["k"], sub["v"], sub["do"], scale, True)
+            compare(got, {n: ref[n][0] for n in ("o", "lse", "dq", "dk", "dv")}, dtype,
+                    f"packed sequence {b} against the oracle")
+            compare((do_[0], dl[0], (dq_[0], dk_[0], dv_[0])), {n: ref[n][0] for n in ("o", "lse", "dq", "dk", "dv")},
+                    dtype, f"dense call of sequence {b} against the oracle")
     rng = np.random.default_rng(5)
     dq_got, dq_ref = [], []
     for b in (0, 2, 4, 9):
