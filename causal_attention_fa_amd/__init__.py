@@ -1,6 +1,6 @@
 """Python binding of libfa.so, the MI355X fused causal attention library.
 
-The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_workspace_bytes``, ``fa_fwd_ex``,
+The functions ``fa_fwd``, ``fa_bwd``, ``fa_bwd_noalloc``, ``fa_bwd_workspace_bytes``, ``fa_fwd_ex``,
 ``fa_bwd_ex``, ``fa_bwd_ex_workspace_bytes`` and ``fa_status_string`` mirror
 the C ABI in ``include/fa.h`` one to one: they take raw device addresses (ints)
 and sizes (or an ``fa_params_t``) and return the C status code.  Every step of
@@ -26,7 +26,8 @@ import os
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP",
     "FA_F32", "FA_F16", "FA_BF16", "FAError", "library_path", "lib",
-    "fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_profile_events",
+    "fa_fwd", "fa_bwd", "fa_bwd_noalloc", "FA_BWD_NOALLOC_MAX_ROWS", "fa_bwd_workspace_bytes",
+    "fa_status_string", "fa_profile_events",
     "fa_params_t", "params", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes",
     "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
     "forward", "backward", "forward_varlen", "backward_varlen", "forward_splitkv", "attention",
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = i
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
         L.fa_bwd.restype = i
+        L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+        L.fa_bwd_noalloc.restype = i
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_bwd_workspace_bytes.restype = sz
         L.fa_status_string.argtypes = [i]
@@ -109,6 +112,14 @@ def fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, S, D, scale, causal, dty
            workspace, workspace_bytes, stream) -> int:
     return lib().fa_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, S, D, scale, int(causal), dtype,
                         workspace, workspace_bytes, stream)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, S, D, scale, causal, dtype, stream) -> int:
+    return lib().fa_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, B, Hq, Hkv, S, D, scale, int(causal), dtype,
+                                stream)
+
+
+FA_BWD_NOALLOC_MAX_ROWS = 1 << 22
 
 
 def fa_bwd_workspace_bytes(B, Hq, Hkv, S, D) -> int:

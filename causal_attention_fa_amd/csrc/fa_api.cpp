@@ -63,6 +63,14 @@ fa_status_t check(const fa_params_t* p, fa::Problem* pb, long long* qrows, long 
   return FA_OK;
 }
 
+// The backward's buffers: those of a side with rows must be present.
+bool bwd_buffers_ok(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+                    const void* dq, const void* dk, const void* dv, long long qrows, long long krows) {
+  if (qrows > 0 && (!present(q) || !present(o) || !present(lse) || !present(dO) || !present(dq))) return false;
+  if (krows > 0 && (!present(k) || !present(v) || !present(dk) || !present(dv))) return false;
+  return true;
+}
+
 // Split-KV plan: nsplit key ranges of `chunk` keys (whole split-kernel tiles).
 // With no request, enough ranges to give the GPU about kSplitTarget
 // workgroups, keeping at least two tiles per range.
@@ -150,9 +158,7 @@ fa_status_t fa_bwd_ex(const void* q, const void* k, const void* v, const void* o
   long long qrows = 0, krows = 0;
   fa_status_t st = check(p, &pb, &qrows, &krows);
   if (st != FA_OK || (qrows == 0 && krows == 0)) return st;
-  if (qrows > 0 && (!present(q) || !present(o) || !present(lse) || !present(dO) || !present(dq)))
-    return FA_ERR_INVALID_ARG;
-  if (krows > 0 && (!present(k) || !present(v) || !present(dk) || !present(dv))) return FA_ERR_INVALID_ARG;
+  if (!bwd_buffers_ok(q, k, v, o, lse, dO, dq, dk, dv, qrows, krows)) return FA_ERR_INVALID_ARG;
   const size_t need = fa_bwd_ex_workspace_bytes(p);
   if (need > 0 && (!workspace || !aligned16(workspace))) return FA_ERR_INVALID_ARG;
   if (workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -204,6 +210,27 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const fa_params_t p = dense(B, Hq, Hkv, S, D, scale, causal, dtype);
   return fa_bwd_ex(q, k, v, o, lse, dO, dq, dk, dv, &p, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dO, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int S, int D,
+                           float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  const fa_params_t p = dense(B, Hq, Hkv, S, D, scale, causal, dtype);
+  fa::Problem pb;
+  long long qrows = 0, krows = 0;
+  fa_status_t st = check(&p, &pb, &qrows, &krows);
+  if (st != FA_OK || (qrows == 0 && krows == 0)) return st;
+  if (!bwd_buffers_ok(q, k, v, o, lse, dO, dq, dk, dv, qrows, krows)) return FA_ERR_INVALID_ARG;
+  if (qrows > FA_BWD_NOALLOC_MAX_ROWS) return FA_ERR_WORKSPACE;
+  static_assert(FA_BWD_NOALLOC_MAX_ROWS == fa::kNoAllocRows, "one size for the static array");
+  // the array's address is per device: the stream must run on the current one
+  int cur = -1, sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+  if (cur != sdev) return FA_ERR_INVALID_ARG;
+  float* rowdot = nullptr;
+  if (fa::noalloc_rowdot(&rowdot) != hipSuccess) return FA_ERR_HIP;
+  fa::BwdArgs a{q, k, v, o, lse, dO, dq, dk, dv, rowdot, pb, D, scale, (int)dtype, g_events, g_nevents};
+  return fa::launch_bwd(a, stream) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

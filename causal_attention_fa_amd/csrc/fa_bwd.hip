@@ -36,9 +36,37 @@
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
+#include <mutex>
 #include <type_traits>
 
 namespace fa {
+
+// ------------------------------------------------------------------ static scratch
+// The row dot products of fa_bwd_noalloc.  Each GPU holds its own copy at its
+// own address; host code reaches it only through the address that
+// hipGetSymbolAddress returns with that GPU current (the array's name on the
+// host is a host-side stand-in, not a device address).
+static __device__ __align__(256) float scratch[kNoAllocRows];
+
+hipError_t noalloc_rowdot(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = static_cast<float*>(addr[dev]);
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------ D = rowsum(dO * O)
 template <typename T, int HD>

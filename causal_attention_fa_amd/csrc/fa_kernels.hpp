@@ -74,6 +74,12 @@ struct SplitArgs {
   int nev;
 };
 
+// Device address, on the current device, of the static row-dot array behind
+// fa_bwd_noalloc (kNoAllocRows fp32 values): looked up on the first request on
+// each device and kept.
+constexpr long long kNoAllocRows = 1LL << 22;
+hipError_t noalloc_rowdot(float** ptr);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream);

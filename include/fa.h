@@ -119,6 +119,30 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    int B, int Hq, int Hkv, int S, int D, float scale, int causal,
                    fa_dtype_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * fa_bwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (without the workspace), results and errors as fa_bwd.  The row
+ * dot products live instead in a static device array of the library,
+ * FA_BWD_NOALLOC_MAX_ROWS fp32 values (16 MiB), one per GPU, held until the
+ * process ends; the call allocates and frees nothing.
+ *   FA_ERR_WORKSPACE    B * Hq * S > FA_BWD_NOALLOC_MAX_ROWS (the static array
+ *                       is too small for the problem; use fa_bwd)
+ *   FA_ERR_INVALID_ARG  also when `stream` belongs to a device other than the
+ *                       calling thread's current device
+ *   FA_ERR_HIP          also when the array's device address cannot be looked
+ *                       up (done once per device, on the first call there)
+ * Every call on one GPU uses that GPU's one array, which keeps the last call's
+ * contents (each call writes every entry it reads).  Calls that overlap on one
+ * GPU (on different streams, or from different host threads without ordering)
+ * race on the array and may return wrong gradients: serialise them.
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS (1 << 22)
+fa_status_t fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dO, void* dq, void* dk, void* dv,
+                           int B, int Hq, int Hkv, int S, int D, float scale, int causal,
+                           fa_dtype_t dtype, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("FA_OK", ...); never NULL.
  * The codes follow the error convention above (an impossible request is an
  * error, not a fallback: udemi.tech "Flash Attention", forcing the flash

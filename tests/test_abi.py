@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert names == ["fa_bwd", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes", "fa_bwd_workspace_bytes", "fa_fwd",
+    assert names == ["fa_bwd", "fa_bwd_ex", "fa_bwd_ex_workspace_bytes", "fa_bwd_noalloc", "fa_bwd_workspace_bytes",
+                     "fa_fwd",
                      "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes", "fa_profile_events",
                      "fa_status_string"]
     L = fa.lib()
@@ -276,3 +277,18 @@ def test_splitkv_shape_limits():
     # no query rows: a no-op that needs no buffers
     assert splitkv(ex_params(Sq=0), q=None, k=None, v=None, o=None, lse=None, workspace=None) == fa.FA_OK
     assert splitkv(ex_params(D=96, Sq=1)) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_noalloc_backward_host_checks():
+    """fa_bwd_noalloc checks its arguments like fa_bwd, and rejects a problem with more
+    query rows than its static array holds, all before any HIP call."""
+    call = lambda **kw: fa.fa_bwd_noalloc(**dict(dict(
+        q=A, k=A, v=A, o=A, lse=A, dO=A, dq=A, dk=A, dv=A, B=1, Hq=4, Hkv=2, S=16, D=64, scale=0.125, causal=1,
+        dtype=fa.FA_BF16, stream=None), **kw))
+    assert call(q=None) == fa.FA_ERR_INVALID_ARG
+    assert call(dv=A + 4) == fa.FA_ERR_INVALID_ARG
+    assert call(Hq=3) == fa.FA_ERR_INVALID_ARG
+    assert call(D=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(B=0) == fa.FA_OK                          # empty: a no-op
+    rows = fa.FA_BWD_NOALLOC_MAX_ROWS
+    assert call(Hq=64, Hkv=64, S=rows // 64 + 1) == fa.FA_ERR_WORKSPACE
