@@ -163,15 +163,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   dold.init(tid);
   float ld_l = 0.f, ld_d = 0.f;
   // (query head, query tile) of an iteration, advanced without divisions.
-  // Query tiles are walked from the last one down: every workgroup of a KV
-  // group then starts on the same tile and they move through Q / dO nearly in
-  // step, so the tiles in use at any time stay few and hit in the XCD's L2.
-  int cur_hq = hkv * G, cur_qt = nqt - 1;    // the tile in LDS buffer `it & 1`
-  int nxt_hq = cur_hq, nxt_qt = cur_qt;      // the tile being prefetched
+  // Query tiles are walked from the last one down, and for each tile the
+  // group's query heads one after another: every workgroup of a KV group
+  // starts on the same tile and they all visit the tiles in the same order
+  // (a workgroup of later keys stops earlier), so the tiles in use at any time
+  // stay few and hit in the XCD's L2.
+  const int hq0 = hkv * G;
+  int cur_hq = hq0, cur_qt = nqt - 1;    // the tile in LDS buffer `it & 1`
+  int nxt_hq = cur_hq, nxt_qt = cur_qt;  // the tile being prefetched
   auto advance = [&](int& hq, int& qt) {
-    if (--qt < first) {
-      qt = nqt - 1;
-      ++hq;
+    if (++hq == hq0 + G) {
+      hq = hq0;
+      --qt;
     }
   };
   // a head's first query row, from the group's first head (no offset loads)
