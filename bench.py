@@ -6,6 +6,7 @@ D=128, bf16, causal) with every input already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-memory] [--no-decode] [--no-sweep]
+                    [--no-configs] [--sweep-ms MS] [--calibrate-copy-mib MIB]
 
 Prints one JSON line.  ``value`` is causal fwd+bwd TFLOP/s: 4*D flops per
 visited (query, key) pair for the forward and 10*D for the backward, pairs =
@@ -13,10 +14,21 @@ B*Hq*S*(S+1)/2, divided by the measured time per step.  Per-kernel durations
 come from HIP events the library records around each of its kernel launches
 (fa_profile_events) during the same timed steps.
 
-Also reported, outside the timed steps: ``forward_sweep`` (the forward alone
-at S = 4096, 8192, 16384 with 32/8 heads, D = 128), ``decode`` (one split-KV
-decode step of 16 sequences x 8192 cached keys, as GB/s against HBM, beside
-the plain forward on the same inputs), ``memory`` and ``cpu_baseline``.
+Per-kernel and per-step times are reported as mean, median and minimum over
+the timed steps.  ``gfx_clock`` holds the GPU's graphics clock (amdsmi GPU
+metrics, mean over the XCDs) sampled while the same step, and then the forward
+alone, run back to back for about a second each, right after the timed steps;
+``pct_of_clock_peak`` prices the throughput against 256 CUs x that clock x 4096
+flop/clk/CU instead of the 2.4 GHz figure.
+
+Also reported, outside the timed steps: ``configs`` (forward and backward of
+each of the five workloads, timed call by call), ``forward_sweep`` (the forward
+alone at S = 4096, 8192, 16384 with 32/8 heads, D = 128), ``decode`` (one
+split-KV decode step of 16 sequences x 8192 cached keys, as GB/s against HBM,
+beside the plain forward on the same inputs), ``memory`` and ``cpu_baseline``.
+Counter figures (HBM bytes, MFMA busy cycles, clock under load) come from the
+committed rocprofv3 profiles of this workload when they were taken on the
+current kernel sources.
 """
 from __future__ import annotations
 
@@ -25,7 +37,9 @@ import ctypes
 import json
 import math
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +51,127 @@ METRIC = "attention fwd+bwd TFLOP/s (causal) and % of bf16 MFMA peak at 1 MI355X
 PEAK_BF16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_FP32_MATRIX_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+CUS = 256                      # MI355X compute units
+BF16_FLOP_PER_CLK_CU = 4096    # dense bf16 / fp16 matrix flops per clock per CU
 KERNELS = ("fwd", "rowdot", "dkdv", "dq")
+
+
+def stats(xs):
+    """mean / median / min of a list of milliseconds."""
+    return {"mean_ms": round(sum(xs) / len(xs), 4), "median_ms": round(statistics.median(xs), 4),
+            "min_ms": round(min(xs), 4)}
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (MHz, the mean over its XCDs) and socket
+    power from a side thread through amdsmi's GPU metrics.  Telemetry only: it
+    reads what the driver reports and changes nothing.  The driver refreshes
+    these metrics only every few hundred milliseconds, so the clock is sampled
+    over a window of about a second of continuous work (``clock_window``), not
+    over the short timed steps.  ``summary()`` says why when there are no
+    samples."""
+
+    def __init__(self, period_s=0.01):
+        self.period = period_s
+        self.clk, self.power = [], []
+        self.max_clk = None
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._h = None
+
+    def _handle(self):
+        import amdsmi
+        hs = amdsmi.amdsmi_get_processor_handles()
+        if len(hs) == 1:
+            return hs[0]
+        import torch
+        props = torch.cuda.get_device_properties(0)
+        bus = getattr(props, "pci_bus_id", None)
+        for h in hs:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)      # "dddd:bb:dd.f"
+            if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                return h
+        raise RuntimeError(f"{len(hs)} GPUs visible to amdsmi and none matched cuda:0")
+
+    def _read(self):
+        import amdsmi
+        m = amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float))]
+        clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
+        w = m.get("current_socket_power")
+        return (float(clk) if isinstance(clk, (int, float)) else None,
+                float(w) if isinstance(w, (int, float)) else None)
+
+    def __enter__(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._h = self._handle()
+            self.max_clk = amdsmi.amdsmi_get_clock_info(self._h, amdsmi.AmdSmiClkType.GFX).get("max_clk")
+            self._read()
+        except Exception as e:  # telemetry is optional
+            self.error = f"{type(e).__name__}: {e}"
+            self._h = None
+            return self
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    c, w = self._read()
+                    if c is not None:
+                        self.clk.append(c)
+                    if w is not None:
+                        self.power.append(w)
+                except Exception as e:
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                time.sleep(self.period)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        try:
+            import amdsmi
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+        return False
+
+    def summary(self):
+        # the first third of the window covers the clock's ramp from idle
+        clk, pw = self.clk[len(self.clk) // 3:], self.power[len(self.power) // 3:]
+        if not clk:
+            return {"samples": 0, "note": self.error or "no samples"}
+        out = {"samples": len(clk), "median_mhz": round(statistics.median(clk), 1), "min_mhz": round(min(clk), 1),
+               "max_mhz": round(max(clk), 1), "max_clk_mhz": self.max_clk}
+        if pw:
+            out["socket_power_w_median"] = round(statistics.median(pw), 1)
+        return out
+
+
+def clock_window(fn, seconds):
+    """The graphics clock while fn() runs back to back for `seconds`."""
+    import torch
+    torch.cuda.synchronize()
+    with ClockSampler() as cs:
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    out = cs.summary()
+    out["seconds"] = seconds
+    out["calls"] = n
+    return out
 
 
 class Hip:
@@ -85,6 +219,20 @@ def algorithmic_work(w):
         "dq": 2.0 * D * pairs,             # dQ (its S / dP recompute is overhead of the split)
         "rowdot": 2.0 * rows * D * elem + 4.0 * rows,   # read O and dO, write D (bytes)
     }
+
+
+def committed_counters(w):
+    """Per-kernel MFMA and clock figures from the committed counter profile of this
+    workload, if it was taken on exactly the current kernel sources (else None)."""
+    from causal_attention_fa_amd.build import source_fingerprint
+    path = os.path.join(ROOT, "profiles", f"mfma_util_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    if prof.get("source_sha256") != source_fingerprint():
+        return None
+    return prof
 
 
 def committed_traffic(w):
@@ -160,21 +308,29 @@ def run_gpu(w, steps, warmup):
     torch.cuda.synchronize()
     total_ms = hip.ms(start, end)
     per = {n: [] for n in KERNELS}
+    per["step"] = []
     for s in range(steps):
         e = evs[s]
         per["fwd"].append(hip.ms(e[0], e[1]))
         per["rowdot"].append(hip.ms(e[2], e[3]))
         per["dkdv"].append(hip.ms(e[3], e[4]))
         per["dq"].append(hip.ms(e[4], e[5]))
+        per["step"].append(hip.ms(e[0], e[5]))
     for row in evs:
         for e in row:
             hip.destroy(e)
     hip.destroy(start)
     hip.destroy(end)
-    kernel_ms = {n: sum(x) / len(x) for n, x in per.items()}
+    def fwd():
+        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), *args, sh)
+        if st != fa.FA_OK:
+            raise fa.FAError(st, "fa_fwd")
+
+    # the graphics clock under this work, outside the timed steps
+    clock = {"fwd_bwd": clock_window(step, 1.5), "forward": clock_window(fwd, 1.0)}
     del t, q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
-    return total_ms / steps, kernel_ms
+    return total_ms / steps, per, clock
 
 
 def _time_calls(fn, steps, warmup, stream, hip, nev=0):
@@ -205,6 +361,88 @@ def _time_calls(fn, steps, warmup, stream, hip, nev=0):
     hip.destroy(start)
     hip.destroy(end)
     return total, gaps
+
+
+def _time_each(fn, n, warmup, stream, hip):
+    """Milliseconds of each of n calls of fn, from events recorded around every call."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(hip.event(), hip.event()) for _ in range(n)]
+    for a, b in evs:
+        hip.record(a, stream)
+        fn()
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    out = [hip.ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    return out
+
+
+def config_table(skip, steps, warmup):
+    """Forward and backward of every workload, each timed call by call on resident
+    inputs: median / min / mean ms, TFLOP/s at the median and % of the dtype's
+    matrix peak (bf16 / fp16 2516.6, fp32 157.3 TFLOP/s)."""
+    import torch
+
+    import causal_attention_fa_amd as fa
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+    hip = Hip()
+    rows = []
+    for w in WORKLOADS.values():
+        if w.name in skip:
+            continue
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+        code = {"bf16": fa.FA_BF16, "f16": fa.FA_F16, "f32": fa.FA_F32}[w.dtype]
+        inp = workload_inputs(w)
+        t = {n: torch.from_numpy(x).to(dev).to(tdt).contiguous() for n, x in inp.items()}
+        del inp
+        q, k, v = t["q"], t["k"], t["v"]
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+        args = (w.B, w.Hq, w.Hkv, w.S, w.D, w.scale, int(w.causal), code)
+        peak = PEAK_FP32_MATRIX_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+
+        def fwd():
+            st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), *args, sh)
+            if st != fa.FA_OK:
+                raise fa.FAError(st, "fa_fwd")
+
+        n = 100 if w.fwd_flops() < 1e11 else steps
+        row = {"workload": w.name, "dtype": w.dtype, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
+               "peak_tflops": peak}
+        ms = _time_each(fwd, n, warmup, sh, hip)
+        row["fwd"] = dict(stats(ms), calls=n)
+        tf = w.fwd_flops() / (statistics.median(ms) * 1e-3) / 1e12
+        row["fwd"].update(tflops=round(tf, 2), pct_of_peak=round(100 * tf / peak, 2))
+        if w.backward:
+            fwd()
+            do = t["do"]
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            nb = fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.S, w.D)
+            ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+
+            def bwd():
+                st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *args, ws.data_ptr(),
+                               ws.numel(), sh)
+                if st != fa.FA_OK:
+                    raise fa.FAError(st, "fa_bwd")
+
+            ms = _time_each(bwd, n, warmup, sh, hip)
+            row["bwd"] = dict(stats(ms), calls=n)
+            tf = w.bwd_flops() / (statistics.median(ms) * 1e-3) / 1e12
+            row["bwd"].update(tflops=round(tf, 2), pct_of_peak=round(100 * tf / peak, 2))
+            del do, dq, dk, dv, ws
+        rows.append(row)
+        del t, q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return rows
 
 
 def decode_bench(steps, warmup):
@@ -254,7 +492,7 @@ def decode_bench(steps, warmup):
             "plain_forward_ms": round(plain_ms, 4), "speedup_vs_plain_forward": round(plain_ms / ms, 2)}
 
 
-def forward_sweep(steps, warmup):
+def forward_sweep(steps, warmup, span_ms=200.0):
     """Forward alone at S = 4096, 8192, 16384 (B=1, Hq=32, Hkv=8, D=128, bf16, causal)."""
     import torch
 
@@ -279,10 +517,10 @@ def forward_sweep(steps, warmup):
             if st != fa.FA_OK:
                 raise fa.FAError(st, "fa_fwd")
 
-        # short kernels: warm up and time for a fixed span (~0.1 s, ~0.2 s), so
-        # that the clock has settled and one launch's overhead does not count
+        # short kernels: warm up and time for a fixed span (span_ms / 2, span_ms),
+        # so that the clock has settled and one launch's overhead does not count
         est, _ = _time_calls(fwd, 3, 1, sh, hip)
-        ms, _ = _time_calls(fwd, max(steps, int(200 / est)), max(warmup, int(100 / est)), sh, hip)
+        ms, _ = _time_calls(fwd, max(steps, int(span_ms / est)), max(warmup, int(span_ms / 2 / est)), sh, hip)
         tf = 4.0 * D * B * Hq * S * (S + 1) / 2 / (ms * 1e-3) / 1e12
         out.append({"S": S, "ms": round(ms, 4), "tflops": round(tf, 1),
                     "pct_of_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)})
@@ -384,6 +622,9 @@ def main():
     ap.add_argument("--no-memory", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the split-KV decode measurement")
     ap.add_argument("--no-sweep", action="store_true", help="skip the forward sweep over S")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--sweep-ms", type=float, default=200.0,
+                    help="time span of each forward-sweep point (shorter for counter runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a reference "
                          "dispatch for scaling HBM byte counters); not part of the timed steps")
@@ -407,7 +648,8 @@ def main():
     if not w.backward:
         raise SystemExit(f"{w.name} is a forward-only workload; bench times fwd+bwd")
 
-    ms_step, kms = run_gpu(w, args.steps, args.warmup)
+    ms_step, per, clock = run_gpu(w, args.steps, args.warmup)
+    kms = {n: sum(per[n]) / len(per[n]) for n in KERNELS}
     work = algorithmic_work(w)
     flops_step = w.fwd_flops() + w.bwd_flops()
     tflops = flops_step / (ms_step * 1e-3) / 1e12
@@ -418,12 +660,11 @@ def main():
         t_s = kms[n] * 1e-3
         if n == "rowdot":
             a = work[n] / t_s / 1e9
-            kernels[n] = {"ms": round(kms[n], 4), "bound": "hbm", "achieved": round(a, 1), "unit": "GB/s",
-                          "frac": round(a / PEAK_HBM_GBS, 4)}
+            kernels[n] = {"bound": "hbm", "achieved": round(a, 1), "unit": "GB/s", "frac": round(a / PEAK_HBM_GBS, 4)}
         else:
             a = work[n] / t_s / 1e12
-            kernels[n] = {"ms": round(kms[n], 4), "bound": "mfma", "achieved": round(a, 1), "unit": "TFLOP/s",
-                          "frac": round(a / peak, 4)}
+            kernels[n] = {"bound": "mfma", "achieved": round(a, 1), "unit": "TFLOP/s", "frac": round(a / peak, 4)}
+        kernels[n].update(ms=round(kms[n], 4), **{k: v for k, v in stats(per[n]).items() if k != "mean_ms"})
     dom = max(KERNELS, key=lambda n: kms[n])
     kd = kernels[dom]
     prof = committed_traffic(w)
@@ -435,6 +676,12 @@ def main():
                 kernels[n]["hbm_bytes"] = t["fetch_bytes"] + t["write_bytes"]
         if dom in prof["kernels"]:
             traffic = prof["kernels"][dom]["fetch_bytes"] + prof["kernels"][dom]["write_bytes"]
+    ctr = committed_counters(w)
+    if ctr is not None:
+        for n in KERNELS:
+            c = ctr["kernels"].get(n)
+            if c is not None:
+                kernels[n]["counters"] = c
     roofline = {"kernel": dom, "bound": kd["bound"], "achieved": kd["achieved"],
                 "peak": PEAK_HBM_GBS if kd["bound"] == "hbm" else peak, "unit": kd["unit"], "frac": kd["frac"],
                 "traffic": traffic,
@@ -444,7 +691,9 @@ def main():
                 if traffic is not None else "no counter profile for the current kernel sources",
                 "work_per_launch": work[dom],
                 "work_note": "fwd 4*D, dkdv 8*D, dq 2*D flops per visited causal pair; rowdot bytes = read O, dO "
-                             "+ write D"}
+                             "+ write D; achieved = work / mean event-timed duration"}
+    bwd_ms = kms["rowdot"] + kms["dkdv"] + kms["dq"]
+    step_stats = stats(per["step"])
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -461,15 +710,30 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
                    "causal": w.causal, "scale": w.scale, "flops_per_step": flops_step},
         "pct_of_bf16_peak": round(100.0 * tflops / peak, 2),
-        "forward": {"ms": round(kms["fwd"], 4), "tflops": kernels["fwd"]["achieved"],
+        "step_kernels": dict(step_stats, tflops_at_median=round(flops_step / (step_stats["median_ms"] * 1e-3) / 1e12,
+                                                                  2),
+                             note="fwd start to dQ end per step, from the library's kernel events"),
+        "forward": {"ms": round(kms["fwd"], 4), "median_ms": kernels["fwd"]["median_ms"],
+                    "min_ms": kernels["fwd"]["min_ms"], "tflops": kernels["fwd"]["achieved"],
                     "pct_of_bf16_peak": round(100.0 * kernels["fwd"]["frac"], 2)},
-        "backward": {"ms": round(kms["rowdot"] + kms["dkdv"] + kms["dq"], 4),
-                     "tflops": round(w.bwd_flops() / ((kms["rowdot"] + kms["dkdv"] + kms["dq"]) * 1e-3) / 1e12, 1)},
+        "backward": {"ms": round(bwd_ms, 4), "tflops": round(w.bwd_flops() / (bwd_ms * 1e-3) / 1e12, 1)},
         "kernels": kernels,
         "roofline": roofline,
+        "gfx_clock": clock,
     }
+    cf, cb = clock["forward"].get("median_mhz"), clock["fwd_bwd"].get("median_mhz")
+    if cf and cb and w.dtype != "f32":
+        def cpeak(mhz):
+            return CUS * mhz * 1e6 * BF16_FLOP_PER_CLK_CU / 1e12
+        out["pct_of_clock_peak"] = {
+            "fwd_bwd": round(100 * tflops / cpeak(cb), 2), "fwd_bwd_clock_mhz": cb,
+            "forward": round(100 * kernels["fwd"]["achieved"] / cpeak(cf), 2), "forward_clock_mhz": cf,
+            "note": "256 CUs x the sampled graphics clock under that work x 4096 bf16 flop/clk/CU; the 2516.6 "
+                    f"TFLOP/s peak assumes {clock['forward'].get('max_clk_mhz')} MHz"}
+    if not args.no_configs:
+        out["configs"] = config_table({w.name}, 20, 5)
     if not args.no_sweep:
-        out["forward_sweep"] = forward_sweep(10, 3)
+        out["forward_sweep"] = forward_sweep(10, 3, args.sweep_ms)
     if not args.no_decode:
         out["decode"] = decode_bench(20, 5)
     if not args.no_memory:
