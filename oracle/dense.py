@@ -29,6 +29,15 @@ With dP = dO V^T:
 and, for GQA, dK / dV of a KV head are the sums over the query heads that read
 it (each query head's use of the shared K/V adds its own term).
 
+Linear position bias (ALiBi, every function's ``alibi`` argument): a list of
+one slope per query head, or None.  With slope a_h, the score of query i and
+key j becomes scale * q_i . k_j - a_h * |i + offset - j| before the mask and
+the softmax (offset = Skv - Sq, so the penalty is 0 on the bottom-right
+diagonal and grows by a_h per key of distance).  "FlashAttention 与 SDPA
+Backend" (section 失败场景与生产实现差距) lists ALiBi in its support matrix
+without defining it; this form (and the slopes as an input) is a reading.  The
+bias is a constant, so the gradients keep their form: dS = P * (dP - D).
+
 Rows are processed in blocks only to bound memory; each row's softmax is always
 taken over all of its unmasked columns at once.  Under a causal mask the columns
 beyond the block's last row are all -inf and contribute exactly zero, so they
@@ -68,13 +77,26 @@ def visible(rows, cols, causal, offset=0, window=None):
     return vis
 
 
-def softmax_probs(q_rows, rows, k_head, scale, causal, offset=0, window=None):
+def alibi_bias(rows, cols, slope, offset=0):
+    """The linear position bias -slope * |i + offset - j| of queries ``rows`` (their
+    positions) and keys ``cols``, shape (len(rows), len(cols))."""
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.asarray(cols, dtype=np.int64)[None, :]
+    return -float(slope) * np.abs(i + offset - j).astype(np.float64)
+
+
+def _slope(alibi, h):
+    return None if alibi is None else float(alibi[h])
+
+
+def softmax_probs(q_rows, rows, k_head, scale, causal, offset=0, window=None, slope=None):
     """Rows of P and L for the query rows ``rows`` (their positions 0..Sq-1).
 
     q_rows: (n, D) query vectors of those rows; k_head: (Skv, D) keys of the
     KV head they read.  Returns (P, L, ncols) where P is (n, ncols): columns at
     or beyond ``ncols`` are all masked (causal) and so P is zero there.
     A row with no visible key gets P = 0 and L = -inf (its softmax is empty).
+    ``slope``: the head's ALiBi slope, or None for no bias.
     """
     rows = np.asarray(rows, dtype=np.int64)
     q_rows = _f64(q_rows)
@@ -86,6 +108,8 @@ def softmax_probs(q_rows, rows, k_head, scale, causal, offset=0, window=None):
     if ncols == 0:
         return np.zeros((n, 0)), np.full(n, -np.inf), 0
     sc = scale * (q_rows @ k_head[:ncols].T)
+    if slope is not None:
+        sc = sc + alibi_bias(rows, np.arange(ncols), slope, offset)
     vis = visible(rows, np.arange(ncols), causal, offset, window)
     sc = np.where(vis, sc, -np.inf)
     any_vis = vis.any(axis=1)
@@ -108,11 +132,12 @@ def _check_shapes(q, k, v):
     return B, Hq, Hkv, Sq, Skv, D
 
 
-def sdpa_forward(q, k, v, scale, causal, heads=None, row_block=512, window=None):
+def sdpa_forward(q, k, v, scale, causal, heads=None, row_block=512, window=None, alibi=None):
     """O [B,Hq,Sq,D] and L [B,Hq,Sq] in fp64 (keys may be longer or shorter: Skv).
 
     ``heads``: optional list of (b, h) to compute; other heads are left NaN.
-    ``window``: optional left window (see ``visible``).
+    ``window``: optional left window (see ``visible``).  ``alibi``: per-head
+    slopes (see the module docstring) or None.
     """
     B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
     off = Skv - Sq
@@ -125,23 +150,23 @@ def sdpa_forward(q, k, v, scale, causal, heads=None, row_block=512, window=None)
         for r0 in range(0, Sq, row_block):
             r1 = min(Sq, r0 + row_block)
             rows = np.arange(r0, r1)
-            P, Lr, nc = softmax_probs(q[b, h, r0:r1], rows, kh, scale, causal, off, window)
+            P, Lr, nc = softmax_probs(q[b, h, r0:r1], rows, kh, scale, causal, off, window, _slope(alibi, h))
             O[b, h, r0:r1] = P @ vh[:nc]
             L[b, h, r0:r1] = Lr
     return O, L
 
 
-def sdpa_forward_rows(q, k, v, scale, causal, b, h, rows, window=None):
+def sdpa_forward_rows(q, k, v, scale, causal, b, h, rows, window=None, alibi=None):
     """O and L of selected rows of one (b, h): ((n, D), (n,)) in fp64."""
     B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
     g = _kv_head(h, Hq, Hkv)
     rows = np.asarray(rows, dtype=np.int64)
-    P, Lr, nc = softmax_probs(q[b, h][rows], rows, k[b, g], scale, causal, Skv - Sq, window)
+    P, Lr, nc = softmax_probs(q[b, h][rows], rows, k[b, g], scale, causal, Skv - Sq, window, _slope(alibi, h))
     return P @ _f64(v[b, g][:nc]), Lr
 
 
-def _row_block_backward(q_blk, rows, do_blk, kh, vh, scale, causal, off=0, window=None):
-    P, Lr, nc = softmax_probs(q_blk, rows, kh, scale, causal, off, window)
+def _row_block_backward(q_blk, rows, do_blk, kh, vh, scale, causal, off=0, window=None, slope=None):
+    P, Lr, nc = softmax_probs(q_blk, rows, kh, scale, causal, off, window, slope)
     do_blk = _f64(do_blk)
     O = P @ vh[:nc]
     dP = do_blk @ vh[:nc].T
@@ -149,13 +174,14 @@ def _row_block_backward(q_blk, rows, do_blk, kh, vh, scale, causal, off=0, windo
     return P, Lr, nc, O, dS
 
 
-def sdpa_backward(q, k, v, do, scale, causal, groups=None, row_block=512, window=None):
+def sdpa_backward(q, k, v, do, scale, causal, groups=None, row_block=512, window=None, alibi=None):
     """Gradients of sum(dO * O) with respect to q, k, v (fp64), plus O and L.
 
     ``groups``: optional list of (b, g) KV heads to compute; the query heads
     reading them are computed in full and everything else is left NaN.
     Keys may be longer or shorter than queries (Skv); ``window`` as in
-    ``visible``.  Returns a dict with keys o, lse, dq, dk, dv.
+    ``visible``; ``alibi`` per-head slopes or None.  Returns a dict with keys
+    o, lse, dq, dk, dv.
     """
     B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
     off = Skv - Sq
@@ -178,7 +204,7 @@ def sdpa_backward(q, k, v, do, scale, causal, groups=None, row_block=512, window
                 r1 = min(Sq, r0 + row_block)
                 rows = np.arange(r0, r1)
                 P, Lr, nc, O, dS = _row_block_backward(
-                    qh[r0:r1], rows, do[b, h, r0:r1], kh, vh, scale, causal, off, window)
+                    qh[r0:r1], rows, do[b, h, r0:r1], kh, vh, scale, causal, off, window, _slope(alibi, h))
                 out["o"][b, h, r0:r1] = O
                 out["lse"][b, h, r0:r1] = Lr
                 out["dq"][b, h, r0:r1] = scale * (dS @ kh[:nc])
@@ -189,14 +215,14 @@ def sdpa_backward(q, k, v, do, scale, causal, groups=None, row_block=512, window
     return out
 
 
-def sdpa_dq_rows(q, k, v, do, scale, causal, b, h, rows, window=None):
+def sdpa_dq_rows(q, k, v, do, scale, causal, b, h, rows, window=None, alibi=None):
     """dQ of selected rows of one (b, h), (n, D) in fp64 (each row needs only its own P and dP)."""
     B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
     g = _kv_head(h, Hq, Hkv)
     rows = np.asarray(rows, dtype=np.int64)
     kh, vh = _f64(k[b, g]), _f64(v[b, g])
     _, _, nc, _, dS = _row_block_backward(q[b, h][rows], rows, do[b, h][rows], kh, vh, scale, causal,
-                                          Skv - Sq, window)
+                                          Skv - Sq, window, _slope(alibi, h))
     return scale * (dS @ kh[:nc])
 
 
@@ -205,7 +231,7 @@ def _seq_slices(cu):
     return [(int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)]
 
 
-def sdpa_forward_varlen(q, k, v, cu_q, cu_k, scale, causal, window=None):
+def sdpa_forward_varlen(q, k, v, cu_q, cu_k, scale, causal, window=None, alibi=None):
     """Packed variable-length batch: q [Hq, Tq, D], k, v [Hkv, Tk, D]; sequence b owns
     query rows cu_q[b]:cu_q[b+1] and keys cu_k[b]:cu_k[b+1] and is attended on its
     own (its offset is its own key length minus its own query length).
@@ -217,12 +243,12 @@ def sdpa_forward_varlen(q, k, v, cu_q, cu_k, scale, causal, window=None):
         if q1 == q0:
             continue
         Ob, Lb = sdpa_forward(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], scale, causal,
-                              window=window)
+                              window=window, alibi=alibi)
         O[:, q0:q1], L[:, q0:q1] = Ob[0], Lb[0]
     return O, L
 
 
-def sdpa_backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal, window=None):
+def sdpa_backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal, window=None, alibi=None):
     """Packed variable-length backward (layouts as ``sdpa_forward_varlen``); dict o, lse, dq, dk, dv."""
     out = {"o": np.zeros(q.shape), "lse": np.full(q.shape[:2], np.nan), "dq": np.zeros(q.shape),
            "dk": np.zeros(k.shape), "dv": np.zeros(v.shape)}
@@ -230,7 +256,7 @@ def sdpa_backward_varlen(q, k, v, do, cu_q, cu_k, scale, causal, window=None):
         if q1 == q0:
             continue
         g = sdpa_backward(q[None, :, q0:q1], k[None, :, k0:k1], v[None, :, k0:k1], do[None, :, q0:q1],
-                          scale, causal, window=window)
+                          scale, causal, window=window, alibi=alibi)
         out["o"][:, q0:q1], out["lse"][:, q0:q1], out["dq"][:, q0:q1] = g["o"][0], g["lse"][0], g["dq"][0]
         out["dk"][:, k0:k1], out["dv"][:, k0:k1] = g["dk"][0], g["dv"][0]
     return out

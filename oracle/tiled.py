@@ -44,6 +44,10 @@ query block that can see it:
 GQA: the query heads of a group are visited inside the KV tile's loop, so dK
 and dV of the shared KV head sum over the group (chain rule; the pages' GQA
 section gives only the forward mapping).
+
+ALiBi (``alibi``: one slope per query head): each tile's scores get
+-slope * |i + offset - j| added before the mask, the reading stated in
+``dense``; it is written out here again, on the tile's own indices.
 """
 from __future__ import annotations
 
@@ -104,7 +108,13 @@ class RowState:
         return out, lse
 
 
-def online_forward(q, k, v, scale, causal, br=64, bc=64, return_state=False, window=None):
+def _tile_bias(q_pos, k_pos, slope, off):
+    """-slope * distance from each query's diagonal position to each key of the tile."""
+    dist = np.abs((q_pos[:, None] + off) - k_pos[None, :])
+    return -slope * dist
+
+
+def online_forward(q, k, v, scale, causal, br=64, bc=64, return_state=False, window=None, alibi=None):
     """Returns O [B,Hq,Sq,D], L [B,Hq,Sq] (fp64); with ``return_state`` also the final
     (m, l, acc) of every row.
 
@@ -133,8 +143,12 @@ def online_forward(q, k, v, scale, causal, br=64, bc=64, return_state=False, win
                 lo = 0 if window is None else max(0, i0 + off - window) // bc * bc
                 for j0 in range(lo, hi, bc):
                     j1 = min(j0 + bc, Skv)
-                    vis = _visible(q_pos, np.arange(j0, j1), causal, off, window)
-                    rows.absorb(scale * (Qblk @ Kh[j0:j1].T), vis, Vh[j0:j1])
+                    k_pos = np.arange(j0, j1)
+                    vis = _visible(q_pos, k_pos, causal, off, window)
+                    logits = scale * (Qblk @ Kh[j0:j1].T)
+                    if alibi is not None:
+                        logits = logits + _tile_bias(q_pos, k_pos, float(alibi[h]), off)
+                    rows.absorb(logits, vis, Vh[j0:j1])
                 O[b, h, i0:i1], L[b, h, i0:i1] = rows.result()
                 for dst, val in zip(state, (rows.m, rows.l, rows.acc)):
                     dst[b, h, i0:i1] = val
@@ -143,7 +157,7 @@ def online_forward(q, k, v, scale, causal, br=64, bc=64, return_state=False, win
     return O, L
 
 
-def online_backward(q, k, v, o, lse, do, scale, causal, br=64, bc=64, window=None):
+def online_backward(q, k, v, o, lse, do, scale, causal, br=64, bc=64, window=None, alibi=None):
     """dQ [B,Hq,Sq,D], dK, dV [B,Hkv,Skv,D] (fp64) from the forward's O and L.
 
     Masks as in ``online_forward``.  For a KV tile only the query blocks that can
@@ -176,6 +190,8 @@ def online_backward(q, k, v, o, lse, do, scale, causal, br=64, bc=64, window=Non
                         dOblk = do[b, h, i0:i1]
                         vis = _visible(np.arange(i0, i1), k_pos, causal, off, window)
                         s = scale * (Qblk @ Kt.T)
+                        if alibi is not None:
+                            s = s + _tile_bias(np.arange(i0, i1), k_pos, float(alibi[h]), off)
                         p = np.zeros_like(s)
                         p[vis] = np.exp((s - lse[b, h, i0:i1, None])[vis])
                         gV += p.T @ dOblk

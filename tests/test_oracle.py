@@ -537,3 +537,143 @@ def test_masks_finite_differences(Sq, Skv, window):
             b = {"dq": (m, k, v), "dk": (q, m, v), "dv": (q, k, m)}[name]
             fd = (f(*a) - f(*b)) / (2 * h)
             assert abs(g[name][ix] - fd) <= 1e-7 * max(1.0, abs(fd)), (name, ix)
+
+
+# ---------------------------------------------------------------- ALiBi (linear position bias)
+#
+# Reading (the SDPA page only lists ALiBi in its support matrix): query i and key j
+# get -a_h * |i + offset - j| added to their scaled score, a_h one slope per query head.
+
+SLOPES4 = [0.5, 0.125, 2.0, 0.0]
+
+
+def test_alibi_zero_slope_is_no_bias():
+    q, k, v, do = rand_qkvdo(1, 4, 2, 23, 8, seed=40)
+    for causal in (True, False):
+        a = oracle.sdpa_backward(q, k, v, do, 0.4, causal, alibi=[0.0] * 4)
+        b = oracle.sdpa_backward(q, k, v, do, 0.4, causal)
+        for n in a:
+            np.testing.assert_array_equal(a[n], b[n])
+        Oa, La = oracle.online_forward(q, k, v, 0.4, causal, 4, 3, alibi=[0.0] * 4)
+        Ob, Lb = oracle.online_forward(q, k, v, 0.4, causal, 4, 3)
+        np.testing.assert_array_equal(Oa, Ob)
+        np.testing.assert_array_equal(La, Lb)
+
+
+@pytest.mark.parametrize("Sq,Skv,causal", [(40, 40, True), (17, 40, True), (40, 40, False), (25, 31, False)])
+def test_alibi_zero_keys_geometric_weights(Sq, Skv, causal):
+    """K = 0 leaves the bias alone in the scores: with r = exp(-a), query i weighs key j
+    by r^|i + offset - j|.  Causal, the visible keys are j <= i + offset, so the weights are
+    1, r, r^2, ... back from the diagonal and L_i = log((1 - r^(n)) / (1 - r)) with n the
+    number of visible keys; non-causal, the two sides of the diagonal add up the same way."""
+    D = 4
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((1, 4, Sq, D))
+    k = np.zeros((1, 4, Skv, D))
+    v = rng.standard_normal((1, 4, Skv, D))
+    off = Skv - Sq
+    O, L = oracle.sdpa_forward(q, k, v, 0.5, causal, alibi=SLOPES4[:3] + [0.3])
+    Ot, Lt = oracle.online_forward(q, k, v, 0.5, causal, 5, 4, alibi=SLOPES4[:3] + [0.3])
+    for h, a in enumerate(SLOPES4[:3] + [0.3]):
+        r = math.exp(-a)
+
+        def geo(n):  # 1 + r + ... + r^(n-1)
+            return (1 - r ** n) / (1 - r)
+
+        for i in range(Sq):
+            d = i + off  # the diagonal key of row i
+            left = min(d, Skv - 1)
+            if causal:
+                z = geo(d + 1)
+                w = {j: r ** (d - j) for j in range(0, d + 1)}
+            else:
+                # keys 0..Skv-1 at distances |d - j|: those left of or on the diagonal and those right of it
+                right = Skv - 1 - d
+                z = r ** (d - left) * geo(left + 1) + (r * geo(right) if right > 0 else 0.0)
+                w = {j: r ** abs(d - j) for j in range(Skv)}
+            np.testing.assert_allclose(L[0, h, i], math.log(z), rtol=1e-13, atol=1e-13)
+            ref_o = sum(wj * v[0, h, j] for j, wj in w.items()) / sum(w.values())
+            np.testing.assert_allclose(O[0, h, i], ref_o, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(Ot[0, h, i], ref_o, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(Lt[0, h, i], math.log(z), rtol=1e-13, atol=1e-13)
+
+
+def _torch_alibi(q, k, v, do, scale, causal, window, slopes):
+    """PyTorch's fp64 SDPA with the bias passed as an additive float mask (-inf where hidden)."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    off = Skv - Sq
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Skv)[None, :]
+    vis = np.ones((Sq, Skv), dtype=bool)
+    if causal:
+        vis &= j <= i + off
+    if window is not None:
+        vis &= j >= i + off - window
+    bias = np.stack([np.where(vis, -a * np.abs(i + off - j), -np.inf) for a in slopes])[None]
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    G = Hq // Hkv
+    out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(G, 1), tv.repeat_interleave(G, 1),
+                                         attn_mask=torch.tensor(bias), scale=scale)
+    out.backward(torch.tensor(do))
+    return {"o": out.detach().numpy(), "dq": tq.grad.numpy(), "dk": tk.grad.numpy(), "dv": tv.grad.numpy()}
+
+
+ALIBI_CASES = [(19, 19, True, None), (19, 19, False, None), (11, 23, True, 5), (23, 11, False, 3), (16, 16, True, 0)]
+
+
+@pytest.mark.parametrize("Sq,Skv,causal,window", ALIBI_CASES)
+def test_alibi_against_torch_fp64(Sq, Skv, causal, window):
+    rng = np.random.default_rng(42 + Sq)
+    q = rng.standard_normal((2, 4, Sq, 8)) * 1.5
+    k = rng.standard_normal((2, 2, Skv, 8))
+    v = rng.standard_normal((2, 2, Skv, 8))
+    do = rng.standard_normal((2, 4, Sq, 8))
+    if causal and Skv < Sq:
+        pytest.skip("rows without keys have no softmax in torch")
+    ref = _torch_alibi(q, k, v, do, 0.35, causal, window, SLOPES4)
+    got = oracle.sdpa_backward(q, k, v, do, 0.35, causal, window=window, alibi=SLOPES4)
+    for n in ("o", "dq", "dk", "dv"):
+        np.testing.assert_allclose(got[n], ref[n], atol=1e-12, rtol=1e-10)
+
+
+@pytest.mark.parametrize("Sq,Skv,causal,window", ALIBI_CASES)
+@pytest.mark.parametrize("br,bc", [(1, 1), (4, 3), (16, 8)])
+def test_alibi_tiled_equals_dense(Sq, Skv, causal, window, br, bc):
+    rng = np.random.default_rng(43 + Skv)
+    q = rng.standard_normal((1, 4, Sq, 4)) * 2
+    k = rng.standard_normal((1, 2, Skv, 4))
+    v = rng.standard_normal((1, 2, Skv, 4))
+    do = rng.standard_normal((1, 4, Sq, 4))
+    g = oracle.sdpa_backward(q, k, v, do, 0.6, causal, window=window, alibi=SLOPES4)
+    O, L = oracle.online_forward(q, k, v, 0.6, causal, br, bc, window=window, alibi=SLOPES4)
+    fin = np.isfinite(g["lse"])
+    np.testing.assert_allclose(O, g["o"], atol=1e-12)
+    np.testing.assert_allclose(L[fin], g["lse"][fin], atol=1e-12)
+    dq, dk, dv = oracle.online_backward(q, k, v, O, L, do, 0.6, causal, br, bc, window=window, alibi=SLOPES4)
+    np.testing.assert_allclose(dq, g["dq"], atol=1e-12)
+    np.testing.assert_allclose(dk, g["dk"], atol=1e-12)
+    np.testing.assert_allclose(dv, g["dv"], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_alibi_finite_differences(causal):
+    q, k, v, do = rand_qkvdo(1, 4, 2, 9, 4, seed=44)
+    scale = 0.5
+
+    def f(q_, k_, v_):
+        return float((oracle.sdpa_forward(q_, k_, v_, scale, causal, alibi=SLOPES4)[0] * do).sum())
+
+    g = oracle.sdpa_backward(q, k, v, do, scale, causal, alibi=SLOPES4)
+    h = 1e-6
+    rng = np.random.default_rng(45)
+    for name, arr in (("dq", q), ("dk", k), ("dv", v)):
+        for _ in range(10):
+            ix = tuple(rng.integers(0, n) for n in arr.shape)
+            plus, minus = arr.copy(), arr.copy()
+            plus[ix] += h
+            minus[ix] -= h
+            args_p = {"dq": (plus, k, v), "dk": (q, plus, v), "dv": (q, k, plus)}[name]
+            args_m = {"dq": (minus, k, v), "dk": (q, minus, v), "dv": (q, k, minus)}[name]
+            fd = (f(*args_p) - f(*args_m)) / (2 * h)
+            assert abs(g[name][ix] - fd) <= 1e-7 * max(1.0, abs(fd)), (name, ix, g[name][ix], fd)

@@ -77,6 +77,43 @@ def _pins_hold(dense, tiled):
     ok &= all(np.allclose(g2[n], ref2[n], atol=1e-10) for n in ref2)
     ok &= np.allclose(O2, ref2["o"], atol=1e-10) and np.allclose(L2, g2["lse"], atol=1e-10)
     ok &= all(np.allclose(a, ref2[n], atol=1e-10) for a, n in zip(t2, ("dq", "dk", "dv")))
+    # linear position bias on the same longer-key windowed problem, against torch with the
+    # bias as an additive float mask
+    slopes = [0.5, 0.125, 2.0, 0.25]
+    bias = np.stack([np.where((j <= i + Skv - Sq) & (j >= i + Skv - Sq - win), -a * np.abs(i + Skv - Sq - j),
+                              -np.inf) for a in slopes])[None]
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q2, k2, v2))
+    out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(2, 1), tv.repeat_interleave(2, 1),
+                                         attn_mask=torch.tensor(bias), scale=scale)
+    out.backward(torch.tensor(do2))
+    ref3 = {"o": out.detach().numpy(), "dq": tq.grad.numpy(), "dk": tk.grad.numpy(), "dv": tv.grad.numpy()}
+    try:
+        with np.errstate(all="ignore"):
+            g3 = dense.sdpa_backward(q2, k2, v2, do2, scale, True, window=win, alibi=slopes)
+            O3, L3 = tiled.online_forward(q2, k2, v2, scale, True, 4, 3, window=win, alibi=slopes)
+            t3 = tiled.online_backward(q2, k2, v2, O3, L3, do2, scale, True, 4, 3, window=win, alibi=slopes)
+    except Exception:
+        return False
+    ok &= all(np.allclose(g3[n], ref3[n], atol=1e-10) for n in ref3)
+    ok &= np.allclose(O3, ref3["o"], atol=1e-10) and np.allclose(L3, g3["lse"], atol=1e-10)
+    ok &= all(np.allclose(a, ref3[n], atol=1e-10) for a, n in zip(t3, ("dq", "dk", "dv")))
+    # the bias without the causal mask (keys on both sides of the diagonal)
+    bias = np.stack([-a * np.abs(i + Skv - Sq - j) for a in slopes])[None]
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q2, k2, v2))
+    out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(2, 1), tv.repeat_interleave(2, 1),
+                                         attn_mask=torch.tensor(bias), scale=scale)
+    out.backward(torch.tensor(do2))
+    ref4 = {"o": out.detach().numpy(), "dq": tq.grad.numpy(), "dk": tk.grad.numpy(), "dv": tv.grad.numpy()}
+    try:
+        with np.errstate(all="ignore"):
+            g4 = dense.sdpa_backward(q2, k2, v2, do2, scale, False, alibi=slopes)
+            O4, L4 = tiled.online_forward(q2, k2, v2, scale, False, 4, 3, alibi=slopes)
+            t4 = tiled.online_backward(q2, k2, v2, O4, L4, do2, scale, False, 4, 3, alibi=slopes)
+    except Exception:
+        return False
+    ok &= all(np.allclose(g4[n], ref4[n], atol=1e-10) for n in ref4)
+    ok &= np.allclose(O4, ref4["o"], atol=1e-10) and np.allclose(L4, g4["lse"], atol=1e-10)
+    ok &= all(np.allclose(a, ref4[n], atol=1e-10) for a, n in zip(t4, ("dq", "dk", "dv")))
     return bool(ok)
 
 
@@ -97,6 +134,10 @@ DENSE_MUTANTS = [
     ("dk[:nc] += scale * (dS.T @ qh[r0:r1])", "dk[:nc] += scale * (P.T @ qh[r0:r1])"),
     ("dv[:nc] += P.T @ _f64(do[b, h, r0:r1])", "dv[:nc] += dS.T @ _f64(do[b, h, r0:r1])"),
     ("return h // (Hq // Hkv)", "return h % Hkv"),
+    ("sc = sc + alibi_bias(rows, np.arange(ncols), slope, offset)", "sc = sc - alibi_bias(rows, np.arange(ncols), slope, offset)"),
+    ("return -float(slope) * np.abs(i + offset - j).astype(np.float64)", "return -float(slope) * np.abs(i - j).astype(np.float64)"),
+    ("return -float(slope) * np.abs(i + offset - j).astype(np.float64)", "return -float(slope) * (i + offset - j).astype(np.float64)"),
+    ("return None if alibi is None else float(alibi[h])", "return None if alibi is None else float(alibi[0])"),
 ]
 
 TILED_MUTANTS = [
@@ -117,6 +158,9 @@ TILED_MUTANTS = [
     ("kv = h // G\n            Kh, Vh", "kv = h % Hkv\n            Kh, Vh"),
     ("weight[vis] = np.exp((logits - self.m[:, None])[vis])", "weight[vis] = np.exp(logits[vis])"),
     ("gV += p.T @ dOblk", "gV += p.T @ dOblk * 0.5"),
+    ("dist = np.abs((q_pos[:, None] + off) - k_pos[None, :])", "dist = np.abs(q_pos[:, None] - k_pos[None, :])"),
+    ("logits = logits + _tile_bias(q_pos, k_pos, float(alibi[h]), off)", "logits = logits + _tile_bias(q_pos, k_pos, float(alibi[kv]), off)"),
+    ("s = s + _tile_bias(np.arange(i0, i1), k_pos, float(alibi[h]), off)", "s = s + _tile_bias(np.arange(i0, i1), k_pos, float(alibi[h]), -off)"),
 ]
 
 
