@@ -50,14 +50,16 @@ class fa_params_t(ctypes.Structure):
         ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
         ("total_q", ctypes.c_int), ("total_k", ctypes.c_int),
         ("dtype", ctypes.c_int),
+        ("alibi_slopes", ctypes.c_void_p),
     ]
 
 
 def params(B, Hq, Hkv, Sq, Skv, D, scale, causal=True, window=None, dtype=FA_BF16,
-           cu_seqlens_q=None, cu_seqlens_k=None, total_q=0, total_k=0) -> fa_params_t:
-    """An fa_params_t; ``window=None`` means no window, cu_seqlens_* are device addresses."""
+           cu_seqlens_q=None, cu_seqlens_k=None, total_q=0, total_k=0, alibi_slopes=None) -> fa_params_t:
+    """An fa_params_t; ``window=None`` means no window, cu_seqlens_* and alibi_slopes
+    (Hq fp32 slopes) are device addresses."""
     return fa_params_t(B, Hq, Hkv, Sq, Skv, D, scale, int(causal), -1 if window is None else int(window),
-                       cu_seqlens_q, cu_seqlens_k, total_q, total_k, dtype)
+                       cu_seqlens_q, cu_seqlens_k, total_q, total_k, dtype, alibi_slopes)
 
 
 class FAError(RuntimeError):
@@ -203,21 +205,34 @@ def _scale(scale, D):
     return 1.0 / math.sqrt(D) if scale is None else float(scale)
 
 
-def forward(q, k, v, scale=None, causal=True, with_lse=True, window=None):
+def _slopes(alibi, Hq, device):
+    """Address of a contiguous fp32 device vector of Hq ALiBi slopes, or None."""
+    if alibi is None:
+        return None
+    torch = _torch()
+    if (not isinstance(alibi, torch.Tensor) or alibi.dtype != torch.float32 or alibi.dim() != 1
+            or alibi.numel() != Hq or not alibi.is_contiguous() or alibi.device != device):
+        raise ValueError("alibi must be a contiguous fp32 vector of Hq slopes on the inputs' device")
+    return alibi.data_ptr()
+
+
+def forward(q, k, v, scale=None, causal=True, with_lse=True, window=None, alibi=None):
     """(o, lse) for device tensors q [B,Hq,Sq,D], k, v [B,Hkv,Skv,D]; lse is fp32 [B,Hq,Sq] or None.
 
-    With Sq == Skv and no window this calls fa_fwd, otherwise fa_fwd_ex (causal
-    diagonal aligned bottom-right; ``window`` keys before the diagonal stay visible)."""
+    With Sq == Skv, no window and no bias this calls fa_fwd, otherwise fa_fwd_ex
+    (causal diagonal aligned bottom-right; ``window`` keys before the diagonal
+    stay visible; ``alibi`` an fp32 device vector of Hq slopes)."""
     torch = _torch()
     B, Hq, Hkv, Sq, Skv, D = _check(q, k, v)
     scale = _scale(scale, D)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if with_lse else None
     ptrs = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse))
-    if Sq == Skv and window is None:
+    if Sq == Skv and window is None and alibi is None:
         st = fa_fwd(*ptrs, B, Hq, Hkv, Sq, D, scale, causal, _dtype_code(q), _stream(q))
     else:
-        p = params(B, Hq, Hkv, Sq, Skv, D, scale, causal, window, _dtype_code(q))
+        p = params(B, Hq, Hkv, Sq, Skv, D, scale, causal, window, _dtype_code(q),
+                   alibi_slopes=_slopes(alibi, Hq, q.device))
         st = fa_fwd_ex(*ptrs, p, _stream(q))
     if st != FA_OK:
         raise FAError(st, "fa_fwd")
@@ -230,7 +245,7 @@ def _workspace(nbytes, workspace, device):
     return workspace
 
 
-def backward(q, k, v, o, lse, do, scale=None, causal=True, workspace=None, window=None):
+def backward(q, k, v, o, lse, do, scale=None, causal=True, workspace=None, window=None, alibi=None):
     """(dq, dk, dv) for the forward's inputs, its outputs o and lse, and dO."""
     torch = _torch()
     B, Hq, Hkv, Sq, Skv, D = _check(q, k, v)
@@ -240,8 +255,9 @@ def backward(q, k, v, o, lse, do, scale=None, causal=True, workspace=None, windo
     if lse.shape != (B, Hq, Sq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be contiguous fp32 [B,Hq,Sq]")
     scale = _scale(scale, D)
-    dense = Sq == Skv and window is None
-    p = params(B, Hq, Hkv, Sq, Skv, D, scale, causal, window, _dtype_code(q))
+    dense = Sq == Skv and window is None and alibi is None
+    p = params(B, Hq, Hkv, Sq, Skv, D, scale, causal, window, _dtype_code(q),
+               alibi_slopes=_slopes(alibi, Hq, q.device))
     workspace = _workspace(fa_bwd_ex_workspace_bytes(p), workspace, q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ptrs = tuple(_ptr(t) for t in (q, k, v, o, lse, do, dq, dk, dv))
@@ -268,18 +284,19 @@ def _check_varlen(q, k, v, cu_q, cu_k):
     return cu_q.numel() - 1, q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2]
 
 
-def _varlen_params(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal, window):
+def _varlen_params(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal, window, alibi=None):
     B, Hq, Hkv, Tq, Tk, D = _check_varlen(q, k, v, cu_q, cu_k)
     return params(B, Hq, Hkv, int(max_q), int(max_k), D, _scale(scale, D), causal, window, _dtype_code(q),
-                  cu_q.data_ptr(), cu_k.data_ptr(), Tq, Tk)
+                  cu_q.data_ptr(), cu_k.data_ptr(), Tq, Tk, _slopes(alibi, Hq, q.device))
 
 
 def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None, causal=True,
-                   window=None):
+                   window=None, alibi=None):
     """Packed batch: q [Hq,total_q,D], k, v [Hkv,total_k,D], cu_seqlens_* int32 [B+1] on the device.
     Returns o [Hq,total_q,D] and lse fp32 [Hq,total_q]; max_seqlen_* bound the per-sequence lengths."""
     torch = _torch()
-    p = _varlen_params(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, window)
+    p = _varlen_params(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, window,
+                       alibi)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     st = fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), p, _stream(q))
@@ -289,10 +306,11 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
 
 
 def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale=None,
-                    causal=True, window=None, workspace=None):
+                    causal=True, window=None, workspace=None, alibi=None):
     """(dq, dk, dv) of a packed batch (layouts as ``forward_varlen``)."""
     torch = _torch()
-    p = _varlen_params(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, window)
+    p = _varlen_params(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale, causal, window,
+                       alibi)
     for t in (o, do):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError("o and dO must match q")

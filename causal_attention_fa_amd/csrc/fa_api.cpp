@@ -31,6 +31,7 @@ fa_status_t check(const fa_params_t* p, fa::Problem* pb, long long* qrows, long 
   if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->Sq < 0 || p->Skv < 0 || p->D < 0) return FA_ERR_INVALID_ARG;
   if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARG;
+  if (p->alibi_slopes != nullptr && !aligned4(p->alibi_slopes)) return FA_ERR_INVALID_ARG;
   const bool packed = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
   if (packed) {
     if (p->cu_seqlens_q == nullptr || p->cu_seqlens_k == nullptr) return FA_ERR_INVALID_ARG;
@@ -59,7 +60,7 @@ fa_status_t check(const fa_params_t* p, fa::Problem* pb, long long* qrows, long 
   const int window = (p->window < 0 || p->window >= p->Skv) ? -1 : p->window;
   *pb = fa::Problem{p->B,       p->Hq,  p->Hkv, p->Sq, p->Skv, p->causal ? 1 : 0, window,
                     packed ? p->cu_seqlens_q : nullptr, packed ? p->cu_seqlens_k : nullptr,
-                    packed ? p->total_q : 0, packed ? p->total_k : 0};
+                    packed ? p->total_q : 0, packed ? p->total_k : 0, p->alibi_slopes};
   return FA_OK;
 }
 
@@ -171,7 +172,7 @@ size_t fa_fwd_splitkv_workspace_bytes(const fa_params_t* p, int num_splits) {
   fa::Problem pb;
   long long qrows = 0, krows = 0;
   if (check(p, &pb, &qrows, &krows) != FA_OK || qrows == 0) return 0;
-  if ((long long)(p->Hq / p->Hkv) * p->Sq > 32) return 0;
+  if ((long long)(p->Hq / p->Hkv) * p->Sq > 32 || p->alibi_slopes != nullptr) return 0;
   return round256((size_t)split_work_floats(p, plan_split(p, num_splits), qrows) * sizeof(float));
 }
 
@@ -183,6 +184,7 @@ fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   if (st != FA_OK || qrows == 0) return st;
   // the query rows of one KV group form one 32-column matrix block
   if ((long long)(p->Hq / p->Hkv) * p->Sq > 32) return FA_ERR_UNSUPPORTED;
+  if (p->alibi_slopes != nullptr) return FA_ERR_UNSUPPORTED;  // no position bias in the split kernels
   if (!present(q) || !present(o) || (lse && !aligned16(lse))) return FA_ERR_INVALID_ARG;
   if (krows > 0 && (!present(k) || !present(v))) return FA_ERR_INVALID_ARG;
   if (!present(workspace)) return FA_ERR_INVALID_ARG;

@@ -21,6 +21,9 @@
 //                  so dQ needs no fp32 atomics either.
 // The split recomputes S and dP in both kernels (7 products per (q, k) pair
 // instead of 5) in exchange for no atomic traffic and deterministic outputs.
+// An optional linear position bias (ALiBi) enters the exponent of P in a
+// compile-time variant of both gradient kernels; the gradient formulas are
+// unchanged, since the bias does not depend on Q, K or V.
 //
 // Layout choices (MI355X-specific):
 //   dkdv: S = Q K^T and dP = dO V^T are formed with the wave's keys as MFMA
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 }
 
 // ------------------------------------------------------------------ dK, dV
-template <typename T, int HD, int BQ, int NW, bool CAUSAL, bool WINDOW>
+template <typename T, int HD, int BQ, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dK, T* __restrict__ dV,
@@ -219,6 +222,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     const bool active = (!CAUSAL || i0 + BQ - 1 + off >= kw0) &&
                         (!WINDOW || i0 + off - pb.window <= kw0 + 31);
     if (active) {
+      // linear position bias of the tile's head, in log2 units
+      const float sl2 = ALIBI ? pb.alibi[cur_hq] * kLog2e : 0.f;
       // S, dP - D (BQ x 32): rows = queries of the tile, columns = this wave's
       // keys; the dP products start from -D of their rows, so dS = P (dP - D)
       // needs one multiply per element
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
       // past the end only feed dK / dV columns that are never stored)
       const bool edge = (CAUSAL && i0 + off < kw0 + 31) ||
                         (WINDOW && i0 + BQ - 1 + off - pb.window > kw0) || (i0 + BQ > sv0.sq);
-      if constexpr (CAUSAL && !WINDOW) {
+      if constexpr (CAUSAL && !WINDOW && !ALIBI) {
         // masked pairs get P = dS = 0 in a branch of their own: with the mask
         // inside the loop the compiler computed it (and selected) every tile
 #pragma unroll
@@ -283,6 +288,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
         }
       } else {
         // (the split form above needs more registers with these masks)
+        // query i0 + 32qb + 8g4 + 4h + e is |i0 + off - mykv + ...| keys from this key
+        const float dl = (float)(i0 + off - mykv + 4 * h);
 #pragma unroll
         for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
@@ -292,7 +299,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * g4 + e;
-              float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c, -lv[e]));
+              float e0 = -lv[e];
+              if constexpr (ALIBI) e0 = fmaf(-sl2, fabsf(dl + (float)(32 * qb + 8 * g4 + e)), e0);
+              float p = __builtin_amdgcn_exp2f(fmaf(s[qb][i], c, e0));
               if (edge) {
                 const int q = i0 + qrow + e;
                 const bool vis = q < sv0.sq && (!CAUSAL || mykv <= q + off) &&
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
 }
 
 // ------------------------------------------------------------------ dQ
-template <typename T, int HD, int BC, int NW, bool CAUSAL, bool WINDOW>
+template <typename T, int HD, int BC, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
 __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dQ, Problem pb, float c,
@@ -376,6 +385,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     }
   }
   const float lq = LSE[qrow] * kLog2e;
+  // linear position bias of the head, in log2 units
+  const float sl2 = ALIBI ? pb.alibi[hq] * kLog2e : 0.f;
   f32x16 ndq;  // -D of the lane's row in every slot: the start of its dP^T products
 #pragma unroll
   for (int i = 0; i < 16; ++i) ndq[i] = -Dd[qrow];
@@ -445,10 +456,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
         }
         // P and dS; the masked form is a branch of its own (a mask inside the
         // loop is computed, and selected, for every tile)
+        // key j0 + 32kb + 4h + e of register i (e = 8(i/4) + i%4) is |dl - e|
+        // keys from this query's diagonal
+        const float dl = (float)(myq + off - j0 - 32 * kb - 4 * h);
         auto elementwise = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, -lq));
+            float e0 = -lq;
+            if constexpr (ALIBI) e0 = fmaf(-sl2, fabsf(dl - (float)(8 * (i >> 2) + (i & 3))), e0);
+            float p = __builtin_amdgcn_exp2f(fmaf(s[i], c, e0));
             if constexpr (decltype(masked)::value) {
               const int kv = j0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
               p = key_visible<CAUSAL, WINDOW>(pb, sv, myq, kv) ? p : 0.f;
@@ -494,19 +510,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
 }
 
 // ------------------------------------------------------------------ launch
-template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW>
+template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
 static void launch_dq_nw(const BwdArgs& a, hipStream_t st, float c) {
   constexpr int BC = 64;
   const Problem& pb = a.pb;
   const int nqt = (pb.Sq + 32 * NW - 1) / (32 * NW);
   dim3 grid(nqt * pb.B * pb.Hq);
   if (grid.x > 0)
-    hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL, WINDOW>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
+    hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL, WINDOW, ALIBI>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dq, pb, c,
                        a.scale, nqt);
 }
 
-template <typename T, int HD, bool CAUSAL, bool WINDOW>
+template <typename T, int HD, bool CAUSAL, bool WINDOW, bool ALIBI>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const Problem& pb = a.pb;
   const long long rows = pb.cu_q != nullptr ? (long long)pb.Hq * pb.Tq : (long long)pb.B * pb.Hq * pb.Sq;
@@ -526,7 +542,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     dim3 grid(nkt * pb.B * pb.Hkv);
     mark(a.ev, a.nev, 1, st);
     if (grid.x > 0)
-      hipLaunchKernelGGL((dkdv_kernel<T, HD, BQ, NW, CAUSAL, WINDOW>), grid, dim3(NW * 64), 0, st, (const T*)a.q, (const T*)a.k,
+      hipLaunchKernelGGL((dkdv_kernel<T, HD, BQ, NW, CAUSAL, WINDOW, ALIBI>), grid, dim3(NW * 64), 0, st, (const T*)a.q, (const T*)a.k,
                          (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dk, (T*)a.dv, pb, c,
                          a.scale, nkt);
     hipError_t e = hipGetLastError();
@@ -537,23 +553,28 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   bool wide = false;
   if constexpr (sizeof(T) == 2) {  // fp32 keeps 4-wave workgroups (no 8-wave instances)
     wide = (long long)((pb.Sq + 255) / 256) * pb.B * pb.Hq >= kWideGrid;
-    if (wide) launch_dq_nw<T, HD, 8, CAUSAL, WINDOW>(a, st, c);
+    if (wide) launch_dq_nw<T, HD, 8, CAUSAL, WINDOW, ALIBI>(a, st, c);
   }
-  if (!wide) launch_dq_nw<T, HD, 4, CAUSAL, WINDOW>(a, st, c);
+  if (!wide) launch_dq_nw<T, HD, 4, CAUSAL, WINDOW, ALIBI>(a, st, c);
   mark(a.ev, a.nev, 3, st);
   return hipGetLastError();
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool ALIBI>
 static hipError_t launch_bwd_m(const BwdArgs& a, hipStream_t st) {
   if (a.pb.window >= 0)
-    return a.pb.causal ? launch_bwd_t<T, HD, true, true>(a, st) : launch_bwd_t<T, HD, false, true>(a, st);
-  return a.pb.causal ? launch_bwd_t<T, HD, true, false>(a, st) : launch_bwd_t<T, HD, false, false>(a, st);
+    return a.pb.causal ? launch_bwd_t<T, HD, true, true, ALIBI>(a, st) : launch_bwd_t<T, HD, false, true, ALIBI>(a, st);
+  return a.pb.causal ? launch_bwd_t<T, HD, true, false, ALIBI>(a, st) : launch_bwd_t<T, HD, false, false, ALIBI>(a, st);
+}
+
+template <typename T, int HD>
+static hipError_t launch_bwd_b(const BwdArgs& a, hipStream_t st) {
+  return a.pb.alibi != nullptr ? launch_bwd_m<T, HD, true>(a, st) : launch_bwd_m<T, HD, false>(a, st);
 }
 
 template <typename T>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
-  return a.D == 64 ? launch_bwd_m<T, 64>(a, st) : launch_bwd_m<T, 128>(a, st);
+  return a.D == 64 ? launch_bwd_b<T, 64>(a, st) : launch_bwd_b<T, 128>(a, st);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {

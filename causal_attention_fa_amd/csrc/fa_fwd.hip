@@ -30,6 +30,8 @@
 //     and the accumulator is rescaled only when a row's max grows by > 2^4;
 //   * the row sum l is taken over exactly the rounded P that multiplies V
 //     (packed dot products with (1, 1) on the vector ALU);
+//   * an optional linear position bias (ALiBi) is added to the scaled scores of
+//     each tile before its row max, in a compile-time variant of the kernel;
 //   * causal: workgroups are launched heaviest (last query tiles) first, a wave
 //     skips KV tiles that lie wholly after its rows (or, with a window, wholly
 //     before them), and the element mask is applied on edge tiles only;
@@ -52,7 +54,7 @@ namespace fa {
 // long-context workload), while 2^8 with an unrounded l does not.
 constexpr float kRescaleLog2 = 4.f;
 
-template <typename T, int HD, int BC, int BS, int NW, bool CAUSAL, bool WINDOW>
+template <typename T, int HD, int BC, int BS, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
 __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, Problem pb, float c, int nqt) {
@@ -83,6 +85,10 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   const int qw0 = i0 + 32 * w;
   const int myq = qw0 + r;
   const int off = sv.off;
+  // linear position bias: the head's slope in log2 units (c s - a |i + off - j|
+  // is then the score the softmax takes, already scaled)
+  const float sl2 = ALIBI ? pb.alibi[hq] * kLog2e : 0.f;
+  const float cs = ALIBI ? 1.f : c;
 
   // rows past the end read row sq-1: their results are never stored
   vec8<T> qf[HD / 16];
@@ -190,12 +196,22 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
               s[kb][i] = vis ? s[kb][i] : -INFINITY;
             }
         }
+        if constexpr (ALIBI) {
+          // key j0 + 32kb + 4h + e of register i (e = 8(i/4) + i%4) is
+          // |myq + off - j| keys from the lane's diagonal
+          const float dl = (float)(myq + off - j0 - 4 * h);
+#pragma unroll
+          for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              s[kb][i] = fmaf(s[kb][i], c, -sl2 * fabsf(dl - (float)(32 * kb + 8 * (i >> 2) + (i & 3))));
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = wave_xor32_max(mx) * c;
+        mx = wave_xor32_max(mx) * cs;
         // Move the reference only when a row's max outgrows it by 2^4 (any lane:
         // the branch is wave-uniform).  O = acc / l is exact for any reference.
         if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleLog2) != 0) {
@@ -211,7 +227,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], c, -ref));
+          for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], cs, -ref));
         // O^T (HD x 32) += V_tile^T P^T ; l += sum of the lane's P
 #pragma unroll
         for (int kt = 0; kt < BC / 16; ++kt) {
@@ -248,7 +264,7 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   }
 }
 
-template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW>
+template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
 static void launch_fwd_nw(const FwdArgs& a, hipStream_t st) {
   // 8-wave workgroups (one per CU) load, synchronise and compute per 128 keys,
   // in two buffers of up to 64 KiB; 4-wave ones (two per CU) per 64 keys.  A
@@ -257,11 +273,11 @@ static void launch_fwd_nw(const FwdArgs& a, hipStream_t st) {
   const int nqt = (a.pb.Sq + BR - 1) / BR;
   dim3 grid(nqt * a.pb.B * a.pb.Hq), block(NW * 64);
   if (grid.x > 0)
-    hipLaunchKernelGGL((fwd_kernel<T, HD, BC, BS, NW, CAUSAL, WINDOW>), grid, block, 0, st, (const T*)a.q,
+    hipLaunchKernelGGL((fwd_kernel<T, HD, BC, BS, NW, CAUSAL, WINDOW, ALIBI>), grid, block, 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.pb, a.scale * kLog2e, nqt);
 }
 
-template <typename T, int HD, bool CAUSAL, bool WINDOW>
+template <typename T, int HD, bool CAUSAL, bool WINDOW, bool ALIBI>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   mark(a.ev, a.nev, 0, st);
   // 16-bit: workgroups of 8 waves (256 query rows; one fits a CU at a time)
@@ -273,23 +289,28 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {  // fp32 keeps 4-wave workgroups (no 8-wave instances)
     const long long n8 = (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq;
     wide = n8 >= ((HD == 128 && a.pb.Sq >= 256) ? kCUs : kWideGrid);
-    if (wide) launch_fwd_nw<T, HD, 8, CAUSAL, WINDOW>(a, st);
+    if (wide) launch_fwd_nw<T, HD, 8, CAUSAL, WINDOW, ALIBI>(a, st);
   }
-  if (!wide) launch_fwd_nw<T, HD, 4, CAUSAL, WINDOW>(a, st);
+  if (!wide) launch_fwd_nw<T, HD, 4, CAUSAL, WINDOW, ALIBI>(a, st);
   mark(a.ev, a.nev, 1, st);
   return hipGetLastError();
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool ALIBI>
 static hipError_t launch_fwd_m(const FwdArgs& a, hipStream_t st) {
   if (a.pb.window >= 0)
-    return a.pb.causal ? launch_fwd_t<T, HD, true, true>(a, st) : launch_fwd_t<T, HD, false, true>(a, st);
-  return a.pb.causal ? launch_fwd_t<T, HD, true, false>(a, st) : launch_fwd_t<T, HD, false, false>(a, st);
+    return a.pb.causal ? launch_fwd_t<T, HD, true, true, ALIBI>(a, st) : launch_fwd_t<T, HD, false, true, ALIBI>(a, st);
+  return a.pb.causal ? launch_fwd_t<T, HD, true, false, ALIBI>(a, st) : launch_fwd_t<T, HD, false, false, ALIBI>(a, st);
+}
+
+template <typename T, int HD>
+static hipError_t launch_fwd_b(const FwdArgs& a, hipStream_t st) {
+  return a.pb.alibi != nullptr ? launch_fwd_m<T, HD, true>(a, st) : launch_fwd_m<T, HD, false>(a, st);
 }
 
 template <typename T>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t st) {
-  return a.D == 64 ? launch_fwd_m<T, 64>(a, st) : launch_fwd_m<T, 128>(a, st);
+  return a.D == 64 ? launch_fwd_b<T, 64>(a, st) : launch_fwd_b<T, 128>(a, st);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st) {

@@ -16,6 +16,7 @@ struct Problem {
   const int* cu_q;    // packed: B + 1 cumulative query offsets (device); nullptr: dense
   const int* cu_k;
   int Tq, Tk;         // packed: rows per head slab of q/o/dq and of k/v/dk/dv
+  const float* alibi; // linear position bias: one slope per query head (device), or nullptr
 };
 
 // One (batch, query head, KV head) sequence.  Rows of its queries are

@@ -175,6 +175,15 @@ const char* fa_status_string(fa_status_t s);
  *   (they size the launch).  The kernels clamp offsets into [0, total] and
  *   lengths to the bounds, so malformed offsets give wrong results, never
  *   accesses outside the described buffers.
+ *
+ *   Linear position bias (ALiBi; "FlashAttention 与 SDPA Backend", section
+ *   失败场景与生产实现差距, lists it in the support matrix of a real kernel):
+ *   with alibi_slopes non-NULL (a device array of Hq fp32 values, 4-byte
+ *   aligned), query i and key j of query head h get -alibi_slopes[h] *
+ *   |i + offset - j| added to their scaled score before the softmax (0 on the
+ *   bottom-right diagonal; the form is this library's reading, the page does
+ *   not define it).  The slopes are read on the device and not checked.  The
+ *   split-KV forward returns FA_ERR_UNSUPPORTED for it.
  */
 typedef struct {
   int B, Hq, Hkv;
@@ -187,6 +196,7 @@ typedef struct {
   const int* cu_seqlens_k;     /* device, B + 1 entries, or NULL */
   int total_q, total_k;        /* packed only: cu_seqlens_q[B], cu_seqlens_k[B] */
   fa_dtype_t dtype;
+  const float* alibi_slopes;   /* device, Hq fp32 slopes, or NULL (no bias); see above */
 } fa_params_t;
 
 /* Forward of an extended problem.  Same outputs and errors as fa_fwd; also
@@ -228,7 +238,8 @@ fa_status_t fa_bwd_ex(const void* q, const void* k, const void* v, const void* o
  *                entry are ignored; two calls in flight need two workspaces
  * FA_ERR_UNSUPPORTED when (Hq / Hkv) * Sq > 32: the query rows of one KV group
  * share one 32-column matrix block, which is what lets the G heads of a group
- * read K and V once.  FA_ERR_WORKSPACE when the workspace is too small, and
+ * read K and V once; also when params->alibi_slopes is not NULL.
+ * FA_ERR_WORKSPACE when the workspace is too small, and
  * FA_ERR_INVALID_ARG when it is NULL or misaligned.  Results match fa_fwd_ex's
  * up to fp32 rounding order and are deterministic for a given split count.
  */

@@ -132,10 +132,12 @@ def test_python_wrappers_need_device_tensors():
 def test_params_struct_layout():
     import ctypes
     P = fa.fa_params_t
-    # int B,Hq,Hkv,Sq,Skv,D; float scale; int causal, window; two pointers; int total_q, total_k; enum dtype
+    # int B,Hq,Hkv,Sq,Skv,D; float scale; int causal, window; two pointers; int total_q, total_k; enum dtype;
+    # a pointer (after 4 bytes of padding)
     assert P.scale.offset == 24 and P.window.offset == 32
     assert P.cu_seqlens_q.offset == 40 and P.cu_seqlens_k.offset == 48
-    assert P.total_q.offset == 56 and P.dtype.offset == 64 and ctypes.sizeof(P) == 72
+    assert P.total_q.offset == 56 and P.dtype.offset == 64
+    assert P.alibi_slopes.offset == 72 and ctypes.sizeof(P) == 80
 
 
 def ex_params(**kw):
@@ -292,3 +294,14 @@ def test_noalloc_backward_host_checks():
     assert call(B=0) == fa.FA_OK                          # empty: a no-op
     rows = fa.FA_BWD_NOALLOC_MAX_ROWS
     assert call(Hq=64, Hkv=64, S=rows // 64 + 1) == fa.FA_ERR_WORKSPACE
+
+
+def test_alibi_host_checks():
+    """Slopes must be 4-byte aligned; the split-KV path has no position bias."""
+    assert fwd_ex(ex_params(alibi_slopes=A + 2)) == fa.FA_ERR_INVALID_ARG
+    assert bwd_ex(ex_params(alibi_slopes=A + 2)) == fa.FA_ERR_INVALID_ARG
+    p = ex_params(Sq=1, Skv=64, alibi_slopes=A)
+    assert fa.fa_fwd_splitkv_workspace_bytes(p, 0) == 0
+    assert fa.fa_fwd_splitkv(A, A, A, A, A, p, 0, A, 1 << 20, None) == fa.FA_ERR_UNSUPPORTED
+    # an empty problem with slopes is still a no-op
+    assert fwd_ex(ex_params(B=0, alibi_slopes=A)) == fa.FA_OK
