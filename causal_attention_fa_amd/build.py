@@ -78,5 +78,27 @@ def build_library(extra_flags=(), verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """The C ABI's host code (fa_api.cpp) with stand-in launchers (fa_host_stubs.cpp:
+    every launch reports an error), compiled by g++ with the address and
+    undefined-behaviour sanitizers into ``out_dir/libfa_host_sanitized.so``.  It has no
+    device code and computes nothing; it exists so that the argument checks can run
+    under the sanitizers on a machine without a GPU.  Load it with the ASan runtime
+    preloaded (``g++ -print-file-name=libasan.so``)."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "libfa_host_sanitized.so")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"),
+           os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_host_stubs.cpp"),
+           "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lamdhip64", "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host sanitizer build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {lib}")
+    return lib
+
+
 if __name__ == "__main__":
     build_library(sys.argv[1:], verbose=True)

@@ -6,6 +6,7 @@
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "fa_kernels.hpp"
 
@@ -21,6 +22,17 @@ constexpr int kMaxLen = 1 << 29;  // longest query or key sequence (keeps i + of
 
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
+// The raw value of an enum argument.  A C caller may pass any int; reading an
+// out-of-range value through the C++ enum type is undefined, so every enum the
+// ABI receives is read as an int first and only then compared.
+static_assert(sizeof(fa_dtype_t) == sizeof(int) && sizeof(fa_status_t) == sizeof(int), "enums are ints");
+template <typename E>
+int raw(const E& e) {
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 thread_local hipEvent_t* g_events = nullptr;
 thread_local int g_nevents = 0;
 
@@ -29,7 +41,8 @@ thread_local int g_nevents = 0;
 fa_status_t check(const fa_params_t* p, fa::Problem* pb, long long* qrows, long long* krows) {
   if (p == nullptr) return FA_ERR_INVALID_ARG;
   if (p->B < 0 || p->Hq < 0 || p->Hkv < 0 || p->Sq < 0 || p->Skv < 0 || p->D < 0) return FA_ERR_INVALID_ARG;
-  if (p->dtype != FA_F32 && p->dtype != FA_F16 && p->dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  const int dt = raw(p->dtype);
+  if (dt != FA_F32 && dt != FA_F16 && dt != FA_BF16) return FA_ERR_INVALID_ARG;
   if (!isfinite(p->scale)) return FA_ERR_INVALID_ARG;
   if (p->alibi_slopes != nullptr && !aligned4(p->alibi_slopes)) return FA_ERR_INVALID_ARG;
   const bool packed = p->cu_seqlens_q != nullptr || p->cu_seqlens_k != nullptr;
@@ -109,7 +122,7 @@ fa_params_t dense(int B, int Hq, int Hkv, int S, int D, float scale, int causal,
   p.scale = scale;
   p.causal = causal;
   p.window = -1;
-  p.dtype = dtype;
+  memcpy(&p.dtype, &dtype, sizeof p.dtype);  // checked later as a raw value
   return p;
 }
 
@@ -123,7 +136,7 @@ void fa_profile_events(hipEvent_t* events, int n) {
 }
 
 const char* fa_status_string(fa_status_t s) {
-  switch (s) {
+  switch (raw(s)) {
     case FA_OK: return "FA_OK";
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";

@@ -38,6 +38,7 @@
 //   operand is a transpose read of the row-major K tile.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
+#include "fa_seq.hpp"
 
 #include <mutex>
 #include <type_traits>

@@ -22,15 +22,15 @@
 // No atomics: the result is deterministic for a given split count.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
+#include "fa_seq.hpp"
 
 namespace fa {
 
 template <typename T>
 struct SplitCfg {
-  // 16-bit: 128-key tiles over 4 waves; fp32 tiles are twice the bytes (and
-  // padded), so 64 keys over 2 waves keep K and V double buffered in LDS
-  static constexpr int NW = sizeof(T) == 2 ? 4 : 2;
-  static constexpr int BC = 32 * NW;
+  static constexpr int kDtype = sizeof(T) == 4 ? 0 : 2;  // fp32, or a 16-bit type
+  static constexpr int NW = split_waves(kDtype);
+  static constexpr int BC = split_tile_keys(kDtype);
 };
 
 template <typename T, int HD, bool CAUSAL, bool WINDOW>
@@ -262,7 +262,6 @@ static hipError_t launch_split_d(const SplitArgs& a, hipStream_t st) {
   return a.D == 64 ? launch_split_m<T, 64>(a, st) : launch_split_m<T, 128>(a, st);
 }
 
-int split_tile_keys(int dtype) { return dtype == 0 ? SplitCfg<float>::BC : SplitCfg<__bf16>::BC; }
 
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t st) {
   switch (a.dtype) {

@@ -43,6 +43,7 @@
 //     so at the same time through one L2.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
+#include "fa_seq.hpp"
 
 namespace fa {
 

@@ -80,9 +80,15 @@ struct SplitArgs {
 constexpr long long kNoAllocRows = 1LL << 22;
 hipError_t noalloc_rowdot(float** ptr);
 
+// Waves of a split-KV workgroup: 16-bit tiles of 128 keys over 4 waves; fp32
+// tiles are twice the bytes (and padded), so 64 keys over 2 waves keep K and
+// V double buffered in LDS.  Each wave takes 32 keys of a tile.
+constexpr int split_waves(int dtype) { return dtype == 0 ? 2 : 4; }
+// keys per split-kernel tile (the unit of a key range)
+constexpr int split_tile_keys(int dtype) { return 32 * split_waves(dtype); }
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_splitkv(const SplitArgs& a, hipStream_t stream);
-int split_tile_keys(int dtype);  // keys per split-kernel tile
 
 }  // namespace fa
