@@ -34,9 +34,9 @@
 //   dO^T and Q^T, come from gfx950's LDS transpose read of the same tiles.  L
 //   and D of the tile's rows are staged in LDS too.  The kernel fits two waves
 //   per SIMD only with each transpose read waited for right before its
-//   product; a variant that reads the next product's fragments ahead (one
-//   wave per SIMD) serves grids of up to three workgroups per CU, where the
-//   second wave per SIMD was missing or the last round ran partly empty.
+//   product.  Small grids take one of two variants: two wave groups sharing
+//   a workgroup's keys (one workgroup per CU or fewer), or reading the next
+//   product's fragments ahead at one wave per SIMD (up to three per CU).
 //   dq: S^T = K Q^T and dP^T = V dO^T put one query row per lane pair (like
 //   the forward), and dS^T is the B operand of dQ^T += K^T dS^T, whose K^T
 //   operand is a transpose read of the row-major K tile.
@@ -100,24 +100,35 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ O, co
 }
 
 // ------------------------------------------------------------------ dK, dV
-template <typename T, int HD, int BQ, int NW, bool CAUSAL, bool WINDOW, bool ALIBI, bool AHEAD>
-__global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
+// NG = 2: two groups of NW waves share the workgroup's keys (wave w and wave
+// w + NW own the same 32 keys) and take alternate (query head, query tile)
+// iterations of the walk, each through its own pair of LDS buffers; at the
+// end the second group's dK, dV partial sums are added to the first's through
+// LDS, in a fixed order.  This doubles the waves a small grid runs with (the
+// keys of a problem give one wave per 32 keys and KV head, which at S = 4096
+// and 8 KV heads is one wave per SIMD).
+template <typename T, int HD, int BQ, int NW, int NG, bool CAUSAL, bool WINDOW, bool ALIBI, bool AHEAD>
+__global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dK, T* __restrict__ dV,
     Problem pb, float c, float scale, int nkt) {
   constexpr int BKV = 32 * NW;
-  constexpr int NT = NW * 64;
+  constexpr int NT = NW * 64;  // threads of one group
   using Tile = RowTile<T, BQ, HD>;
   constexpr int kOffQ = 0;
   constexpr int kOffD = Tile::kElems;
   constexpr int kElems = 2 * Tile::kElems;
   using VTile = RowTile<T, BKV, HD>;
-  __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
+  static_assert(NG == 1 || NG == 2, "one or two wave groups");
+  __shared__ __attribute__((aligned(16))) T lds[NG * 2 * kElems];   // [group][buf] Q, dO tiles
   __shared__ __attribute__((aligned(16))) T lds_v[VTile::kElems];  // this workgroup's V rows
-  __shared__ __attribute__((aligned(16))) float lds_ld[2][2][BQ];  // [buf][L*log2e, -D][row]
+  __shared__ __attribute__((aligned(16))) float lds_ld[NG][2][2][BQ];  // [group][buf][L*log2e, -D][row]
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
+  const int w = wv % NW;                                    // the wave's 32 keys
+  const int grp = wv / NW;                                  // its group
+  const int gtid = tid % NT;                                // thread index within the group
   const int lane = tid & 63, r = lane & 31, h = lane >> 5;
   // work item: (b*Hkv + hkv) major, key tiles in order within a group (small
   // key tiles see the most queries: launched first); one XCD takes a
@@ -146,7 +157,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     for (int t = 0; t < HD / 16; ++t) kf[t] = load8<T>(Kh + o + 16 * t);
   }
   {
-    TileLoader<T, BKV, HD, NT> vld;
+    TileLoader<T, BKV, HD, NG * NT> vld;
     vld.init(tid);
     vld.issue(Vh, kv0, sv0.skv, lds_v, tid);
     vld.land(tid);  // published by the first barrier below
@@ -167,8 +178,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   const int total = G * per_head;
 
   LoopLoader<T, BQ, HD, NT> qld, dold;
-  qld.init(tid);
-  dold.init(tid);
+  qld.init(gtid);
+  dold.init(gtid);
   float ld_l = 0.f, ld_d = 0.f;
   // (query head, query tile) of an iteration, advanced without divisions.
   // Query tiles are walked from the last one down, and for each tile the
@@ -177,14 +188,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
   // (a workgroup of later keys stops earlier), so the tiles in use at any time
   // stay few and hit in the XCD's L2.
   const int hq0 = hkv * G;
-  int cur_hq = hq0, cur_qt = nqt - 1;    // the tile in LDS buffer `it & 1`
-  int nxt_hq = cur_hq, nxt_qt = cur_qt;  // the tile being prefetched
   auto advance = [&](int& hq, int& qt) {
     if (++hq == hq0 + G) {
       hq = hq0;
       --qt;
     }
   };
+  // a group takes iterations grp, grp + NG, grp + 2 NG, ... of the walk
+  int cur_hq = hq0, cur_qt = nqt - 1;  // the tile in the group's LDS buffer `step & 1`
+  if (grp == 1) advance(cur_hq, cur_qt);
+  int nxt_hq = cur_hq, nxt_qt = cur_qt;  // the tile being prefetched
+  const int mine = total > grp ? (total - grp + NG - 1) / NG : 0;  // this group's iterations
+  const int steps = (total + NG - 1) / NG;                         // every group's loop count
   // a head's first query row, from the group's first head (no offset loads)
   const size_t hstride = q_head_stride(pb);
   // L and D of the tile's rows: every lane loads one (lanes past BQ repeat a
@@ -195,36 +210,38 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
     const size_t row = q_row0 + min(i0 + (tid & (BQ - 1)), sv0.sq - 1);
     ld_l = LSE[row];
     ld_d = Dd[row];
-    T* base = lds + buf * kElems;
-    qld.issue(Q + q_row0 * HD, i0, sv0.sq, base + kOffQ, tid);
-    dold.issue(dO + q_row0 * HD, i0, sv0.sq, base + kOffD, tid);
+    T* base = lds + (grp * 2 + buf) * kElems;
+    qld.issue(Q + q_row0 * HD, i0, sv0.sq, base + kOffQ, gtid);
+    dold.issue(dO + q_row0 * HD, i0, sv0.sq, base + kOffD, gtid);
   };
   auto commit = [&](int buf) {
-    qld.land(tid);
-    dold.land(tid);
-    if (tid < BQ) {
-      lds_ld[buf][0][tid] = ld_l * kLog2e;
-      lds_ld[buf][1][tid] = -ld_d;
+    qld.land(gtid);
+    dold.land(gtid);
+    if (gtid < BQ) {
+      lds_ld[grp][buf][0][gtid] = ld_l * kLog2e;
+      lds_ld[grp][buf][1][gtid] = -ld_d;
     }
   };
 
-  if (total > 0) {
+  if (mine > 0) {
     issue(cur_hq, cur_qt * BQ, 0);
     commit(0);
   }
   __syncthreads();
-  for (int it = 0; it < total; ++it) {
+  for (int it = 0; it < steps; ++it) {
     const int buf = it & 1;
     const int i0 = cur_qt * BQ;
-    const bool more = it + 1 < total;
+    const bool more = it + 1 < mine;
     if (more) {  // the other buffer was last read before the previous barrier
-      advance(nxt_hq, nxt_qt);
+#pragma unroll
+      for (int k = 0; k < NG; ++k) advance(nxt_hq, nxt_qt);
       issue(nxt_hq, nxt_qt * BQ, buf ^ 1);
     }
-    const T* Qs = lds + buf * kElems + kOffQ;
-    const T* dOs = lds + buf * kElems + kOffD;
-    // does a query of the tile see one of this wave's keys?
-    const bool active = (!CAUSAL || i0 + BQ - 1 + off >= kw0) &&
+    const T* Qs = lds + (grp * 2 + buf) * kElems + kOffQ;
+    const T* dOs = lds + (grp * 2 + buf) * kElems + kOffD;
+    // does a query of the tile see one of this wave's keys?  (a group with
+    // one iteration fewer sits out the last step)
+    const bool active = it < mine && (!CAUSAL || i0 + BQ - 1 + off >= kw0) &&
                         (!WINDOW || i0 + off - pb.window <= kw0 + 31);
     if (active) {
       // linear position bias of the tile's head, in log2 units
@@ -238,7 +255,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
         f32x16 nd;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&lds_ld[buf][1][32 * qb + 8 * g4 + 4 * h]);
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&lds_ld[grp][buf][1][32 * qb + 8 * g4 + 4 * h]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) nd[4 * g4 + e] = x[e];
         }
@@ -271,7 +288,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int qrow = 32 * qb + 8 * g4 + 4 * h;  // first of 4 consecutive query rows
-            const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][0][qrow]);
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[grp][buf][0][qrow]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * g4 + e;
@@ -300,7 +317,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int qrow = 32 * qb + 8 * g4 + 4 * h;
-            const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[buf][0][qrow]);
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(&lds_ld[grp][buf][0][qrow]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * g4 + e;
@@ -342,8 +359,42 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(
       }
     }
     if (more) commit(buf ^ 1);
-    advance(cur_hq, cur_qt);
+#pragma unroll
+    for (int k = 0; k < NG; ++k) advance(cur_hq, cur_qt);
     __syncthreads();
+  }
+
+  if constexpr (NG == 2) {
+    // dK, dV of the two groups: the second group's partial sums go through
+    // the (now free) tile buffers, one accumulator set at a time, and the
+    // first group adds them to its own
+    static_assert(NW * (HD / 32) * 16 * 64 * 4 <= (int)sizeof(lds), "a group's accumulators fit the tile buffers");
+    f32x4* xf = reinterpret_cast<f32x4*>(lds);
+    auto fold = [&](f32x16(&acc)[HD / 32]) __attribute__((always_inline)) {
+      if (grp == 1) {
+#pragma unroll
+        for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            xf[((w * (HD / 32) + d) * 4 + g) * 64 + lane] =
+                f32x4{acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 x = xf[((w * (HD / 32) + d) * 4 + g) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[d][4 * g + e] += x[e];
+          }
+      }
+      __syncthreads();
+    };
+    fold(dk);
+    fold(dv);
+    if (grp != 0) return;
   }
 
   if (mykv < sv0.skv) {
@@ -538,9 +589,9 @@ static void launch_dq_nw(const BwdArgs& a, hipStream_t st, float c) {
                        a.scale, nqt);
 }
 
-template <typename T, int HD, int BQ, int NW, bool CAUSAL, bool WINDOW, bool ALIBI, bool AHEAD>
+template <typename T, int HD, int BQ, int NW, int NG, bool CAUSAL, bool WINDOW, bool ALIBI, bool AHEAD>
 static void launch_dkdv(const BwdArgs& a, hipStream_t st, dim3 grid, float c, int nkt) {
-  hipLaunchKernelGGL((dkdv_kernel<T, HD, BQ, NW, CAUSAL, WINDOW, ALIBI, AHEAD>), grid, dim3(NW * 64), 0, st,
+  hipLaunchKernelGGL((dkdv_kernel<T, HD, BQ, NW, NG, CAUSAL, WINDOW, ALIBI, AHEAD>), grid, dim3(NG * NW * 64), 0, st,
                      (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot,
                      (T*)a.dk, (T*)a.dv, a.pb, c, a.scale, nkt);
 }
@@ -564,14 +615,26 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int nkt = (pb.Skv + 32 * NW - 1) / (32 * NW);
     dim3 grid(nkt * pb.B * pb.Hkv);
     mark(a.ev, a.nev, 1, st);
-    // Up to three workgroups per CU: the read-ahead variant (one wave per
-    // SIMD).  Measured: +13 % on the backward at one workgroup per CU, +2 % at
-    // three; at four (two full rounds of two) the variant loses 9 %.
+    // Small grids (measured on the backward, against the plain kernel):
+    //   up to one workgroup per CU: two wave groups per workgroup (+35 % at
+    //     S = 4096 with 32/8 heads; ALiBi's extra registers do not fit it);
+    //   up to three: the read-ahead variant, one wave per SIMD (+13 % at one
+    //     workgroup per CU, +2 % at three; at four it loses 9 %).
     if (grid.x > 0) {
-      if (sizeof(T) == 2 && (long long)grid.x <= 3 * kCUs)
-        launch_dkdv<T, HD, BQ, NW, CAUSAL, WINDOW, ALIBI, sizeof(T) == 2>(a, st, grid, c, nkt);
-      else
-        launch_dkdv<T, HD, BQ, NW, CAUSAL, WINDOW, ALIBI, false>(a, st, grid, c, nkt);
+      bool done = false;
+      if constexpr (sizeof(T) == 2) {
+        if constexpr (!ALIBI) {
+          if ((long long)grid.x <= kCUs) {
+            launch_dkdv<T, HD, BQ, NW, 2, CAUSAL, WINDOW, ALIBI, false>(a, st, grid, c, nkt);
+            done = true;
+          }
+        }
+        if (!done && (long long)grid.x <= 3 * kCUs) {
+          launch_dkdv<T, HD, BQ, NW, 1, CAUSAL, WINDOW, ALIBI, true>(a, st, grid, c, nkt);
+          done = true;
+        }
+      }
+      if (!done) launch_dkdv<T, HD, BQ, NW, 1, CAUSAL, WINDOW, ALIBI, false>(a, st, grid, c, nkt);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

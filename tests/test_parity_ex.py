@@ -159,7 +159,8 @@ def test_varlen_matches_dense_calls():
     """At full size (16401 packed tokens, 32 query / 8 KV heads, D = 128, bf16): every
     sequence of the packed call matches a dense call on that sequence alone.  Where the
     dense call runs the same kernels (8-wave forward tiles of 128 keys: 2048 tokens or
-    more at 32 heads) the two agree bit for bit, which also rules out a single key
+    more at 32 heads) the two agree bit for bit (dK, dV of a small dense grid to within
+    one bf16 step: see below), which also rules out a single key
     leaking across a sequence boundary; shorter sequences run the 4-wave forward, whose
     64-key tiles round differently; there both calls meet the oracle's bounds.  Sampled
     rows of long and short sequences meet the oracle, and so do whole short sequences."""
@@ -176,9 +177,25 @@ def test_varlen_matches_dense_calls():
         do_, dl, (dq_, dk_, dv_) = run_dense(sub, dtype, scale, True, None)
         got = (o[:, r0:r1], lse[:, r0:r1], (dq[:, r0:r1], dk[:, r0:r1], dv[:, r0:r1]))
         if lens[b] >= 2048:
-            for name, a, ref in (("o", got[0], do_[0]), ("lse", got[1], dl[0]), ("dq", got[2][0], dq_[0]),
-                                 ("dk", got[2][1], dk_[0]), ("dv", got[2][2], dv_[0])):
+            for name, a, ref in (("o", got[0], do_[0]), ("lse", got[1], dl[0]), ("dq", got[2][0], dq_[0])):
                 assert np.array_equal(a, ref), f"sequence {b} {name} differs from the dense call"
+            # The dense call's dK/dV kernel splits each workgroup's query tiles between two
+            # wave groups when its grid (128-key tiles x KV heads) has at most 256
+            # workgroups, one per CU; dK and dV are then the sum of two fp32 partial sums
+            # instead of one running sum.  The order changes the fp32 rounding (relative to
+            # the terms, which can be far larger than a cancelling result) and so, here and
+            # there, the bf16 value: the two must agree to half a bf16 step of the tensor's
+            # largest value and to 1e-3 in rel-L2.  Otherwise the kernels match bit for bit.
+            split = -(-lens[b] // 128) * Hkv <= 256
+            for name, a, ref in (("dk", got[2][1], dk_[0]), ("dv", got[2][2], dv_[0])):
+                if not split:
+                    assert np.array_equal(a, ref), f"sequence {b} {name} differs from the dense call"
+                else:
+                    a64, r64 = a.astype(np.float64), ref.astype(np.float64)
+                    worst = float(np.abs(a64 - r64).max())
+                    assert worst <= 2.0 ** -8 * float(np.abs(r64).max()), f"sequence {b} {name}: max diff {worst:.3g}"
+                    e = rel_l2(a64, r64)
+                    assert e <= 1e-3, f"sequence {b} {name}: rel-L2 {e:.3g} against the dense call"
         else:
             # the dense call takes other kernels here, so both are held to the oracle
             ref = oracle.sdpa_backward(sub["q"], sub["k"], sub["v"], sub["do"], scale, True)
