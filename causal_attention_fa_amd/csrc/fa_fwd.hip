@@ -55,12 +55,19 @@ namespace fa {
 // long-context workload), while 2^8 with an unrounded l does not.
 constexpr float kRescaleLog2 = 4.f;
 
-template <typename T, int HD, int BC, int BS, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
-__global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
+// NG = 2: two groups of NW waves share the workgroup's query rows (waves w and
+// w + NW own the same 32 rows) and take alternate KV stages, each with its own
+// online-softmax state and its own pair of LDS buffers; at the end the second
+// group's (m, l, O) is merged into the first's by the logsumexp identity,
+// through LDS, in a fixed order.  This doubles the waves of a small grid
+// (32 query rows per wave give one wave per SIMD at 8 heads of 4096 rows).
+template <typename T, int HD, int BC, int BS, int NW, int NG, bool CAUSAL, bool WINDOW, bool ALIBI>
+__global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, T* __restrict__ O,
     float* __restrict__ LSE, Problem pb, float c, int nqt) {
   constexpr int BR = 32 * NW;
-  constexpr int NT = NW * 64;
+  constexpr int NT = NW * 64;  // threads of one group
+  static_assert(NG == 1 || (NG == 2 && NW == 4), "two groups of four waves");
   using Tile = RowTile<T, BC, HD>;   // the unit of the products: BC keys
   using Stage = RowTile<T, BS, HD>;  // the unit of the loads and barriers: BS keys
   constexpr int kSub = BS / BC;
@@ -69,10 +76,12 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   // the stage loop unrolled by two: a lane's K (or V) fragments of either
   // buffer are one register each plus a constant offset below 64 KiB.
   constexpr int kVOff = 2 * Stage::kElems;
-  __shared__ __attribute__((aligned(16))) T lds[2 * kVOff];
+  __shared__ __attribute__((aligned(16))) T lds[NG * 2 * kVOff];  // [group] K0, K1, V0, V1
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int w = (tid >> 6) & (NW - 1), lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / NW;  // the wave's group
+  const int gtid = tid & (NT - 1);                                                  // thread within it
   // work item: KV group major, then query tile (heaviest first), then the
   // group's heads; one XCD takes a contiguous run of work items
   const QTile wt = qtile_of<CAUSAL>(xcd_slice(blockIdx.x, gridDim.x), nqt, pb);
@@ -117,15 +126,19 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   // issues loads waits until the memory pipeline has taken them, and the
   // other wave of its SIMD keeps the matrix core busy meanwhile.
   constexpr int NTL = NW == 8 ? NT / 2 : NT;
-  const bool loader = __builtin_amdgcn_readfirstlane(tid >> 6) < NTL / 64;
+  const bool loader = (__builtin_amdgcn_readfirstlane(tid >> 6) & (NW - 1)) < NTL / 64;
   LoopLoader<T, BS, HD, NTL> kld, vld;
-  kld.init(tid);
-  vld.init(tid);
-  if (nstages > 0 && loader) {
-    kld.issue(Kh, jt0 * BS, sv.skv, lds, tid);
-    vld.issue(Vh, jt0 * BS, sv.skv, lds + kVOff, tid);
-    kld.land(tid);
-    vld.land(tid);
+  kld.init(gtid);
+  vld.init(gtid);
+  // a group takes stages grp, grp + NG, ... of the tile's range, in its own buffers
+  T* const gl = lds + grp * 2 * kVOff;
+  const int mine = nstages > grp ? (nstages - grp + NG - 1) / NG : 0;  // this group's stages
+  const int steps = (nstages + NG - 1) / NG;                         // every group's loop count
+  if (mine > 0 && loader) {
+    kld.issue(Kh, (jt0 + grp) * BS, sv.skv, gl, gtid);
+    vld.issue(Vh, (jt0 + grp) * BS, sv.skv, gl + kVOff, gtid);
+    kld.land(gtid);
+    vld.land(gtid);
   }
   __syncthreads();
   // Q has landed too (the loads above waited for it): a wait the compiler
@@ -142,15 +155,16 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   // (the K stages; each V stage sits kVOff further on).
   // The waves synchronise once per stage; within it each wave runs through
   // the stage's tiles at its own pace.
-  auto stage = [&](const int it, const T* cur, T* nxt) __attribute__((always_inline)) {
-    const int s0 = (jt0 + it) * BS;
-    const bool more = it + 1 < nstages;
+  auto stage = [&](const int li, const T* cur, T* nxt) __attribute__((always_inline)) {
+    const int s0 = (jt0 + li * NG + grp) * BS;
+    const bool more = li + 1 < mine;
     if (more && loader) {  // the other buffer was last read before the previous barrier
-      kld.issue(Kh, s0 + BS, sv.skv, nxt, tid);
-      vld.issue(Vh, s0 + BS, sv.skv, nxt + kVOff, tid);
+      kld.issue(Kh, s0 + NG * BS, sv.skv, nxt, gtid);
+      vld.issue(Vh, s0 + NG * BS, sv.skv, nxt + kVOff, gtid);
     }
+    // (a group with one stage fewer sits out the last step)
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub) {
+    for (int sub = 0; sub < kSub && (NG == 1 || li < mine); ++sub) {
       const int j0 = s0 + sub * BC;
       const T* Ks = cur + sub * Tile::kElems;
       const T* Vs = cur + voff + sub * Tile::kElems;
@@ -240,14 +254,48 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
       }
     }
     if (more && loader) {
-      kld.land(tid);
-      vld.land(tid);
+      kld.land(gtid);
+      vld.land(gtid);
     }
     __syncthreads();
   };
-  for (int it = 0; it < nstages; it += 2) {
-    stage(it, lds, lds + Stage::kElems);
-    if (it + 1 < nstages) stage(it + 1, lds + Stage::kElems, lds);
+  for (int li = 0; li < steps; li += 2) {
+    stage(li, gl, gl + Stage::kElems);
+    if (li + 1 < steps) stage(li + 1, gl + Stage::kElems, gl);
+  }
+
+  if constexpr (NG == 2) {
+    // the second group's reference, lane sum and accumulators, through the
+    // (now free) stage buffers; the first group rescales both to the larger
+    // reference and adds them
+    static_assert(NW * (HD / 32 + 1) * 16 * 64 * 4 <= (int)sizeof(lds), "a group's state fits the stage buffers");
+    f32x4* xf = reinterpret_cast<f32x4*>(lds);
+    const int base = w * (HD / 32 * 4 + 1) * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          xf[base + (d * 4 + g) * 64] = f32x4{oacc[d][4 * g], oacc[d][4 * g + 1], oacc[d][4 * g + 2], oacc[d][4 * g + 3]};
+      xf[base + HD / 32 * 4 * 64] = f32x4{m, lsum, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const f32x4 ml = xf[base + HD / 32 * 4 * 64];
+    const float mm = fmaxf(m, ml[0]);
+    // a group that saw no key of these rows has m = -inf and weight 0
+    const float a0 = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mm);
+    const float a1 = ml[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[0] - mm);
+    lsum = lsum * a0 + ml[1] * a1;
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = xf[base + (d * 4 + g) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[d][4 * g + e] = oacc[d][4 * g + e] * a0 + x[e] * a1;
+      }
+    m = mm;
   }
 
   const float l = wave_xor32_sum(lsum);
@@ -265,16 +313,16 @@ __global__ __launch_bounds__(NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_kernel(
   }
 }
 
-template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
+template <typename T, int HD, int NW, int NG, bool CAUSAL, bool WINDOW, bool ALIBI>
 static void launch_fwd_nw(const FwdArgs& a, hipStream_t st) {
   // 8-wave workgroups (one per CU) load, synchronise and compute per 128 keys,
   // in two buffers of up to 64 KiB; 4-wave ones (two per CU) per 64 keys.  A
   // 128-key tile takes one row max, exchange and rescale test per 128 keys.
   constexpr int BS = (NW == 8 && sizeof(T) == 2) ? 128 : 64, BC = BS, BR = 32 * NW;
   const int nqt = (a.pb.Sq + BR - 1) / BR;
-  dim3 grid(nqt * a.pb.B * a.pb.Hq), block(NW * 64);
+  dim3 grid(nqt * a.pb.B * a.pb.Hq), block(NG * NW * 64);
   if (grid.x > 0)
-    hipLaunchKernelGGL((fwd_kernel<T, HD, BC, BS, NW, CAUSAL, WINDOW, ALIBI>), grid, block, 0, st, (const T*)a.q,
+    hipLaunchKernelGGL((fwd_kernel<T, HD, BC, BS, NW, NG, CAUSAL, WINDOW, ALIBI>), grid, block, 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.pb, a.scale * kLog2e, nqt);
 }
 
@@ -290,9 +338,19 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {  // fp32 keeps 4-wave workgroups (no 8-wave instances)
     const long long n8 = (long long)((a.pb.Sq + 255) / 256) * a.pb.B * a.pb.Hq;
     wide = n8 >= ((HD == 128 && a.pb.Sq >= 256) ? kCUs : kWideGrid);
-    if (wide) launch_fwd_nw<T, HD, 8, CAUSAL, WINDOW, ALIBI>(a, st);
+    if (wide) launch_fwd_nw<T, HD, 8, 1, CAUSAL, WINDOW, ALIBI>(a, st);
   }
-  if (!wide) launch_fwd_nw<T, HD, 4, CAUSAL, WINDOW, ALIBI>(a, st);
+  if (!wide) {
+    // 16-bit grids of one 4-wave workgroup per CU or fewer: two wave groups per
+    // workgroup split each tile's KV stages (two waves per SIMD instead of one)
+    bool split = false;
+    if constexpr (sizeof(T) == 2) {
+      const long long n4 = (long long)((a.pb.Sq + 127) / 128) * a.pb.B * a.pb.Hq;
+      split = n4 <= kCUs;
+      if (split) launch_fwd_nw<T, HD, 4, 2, CAUSAL, WINDOW, ALIBI>(a, st);
+    }
+    if (!split) launch_fwd_nw<T, HD, 4, 1, CAUSAL, WINDOW, ALIBI>(a, st);
+  }
   mark(a.ev, a.nev, 1, st);
   return hipGetLastError();
 }
