@@ -413,21 +413,29 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
 }
 
 // ------------------------------------------------------------------ dQ
-template <typename T, int HD, int BC, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
-__global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
+// NG = 2: two groups of NW waves share the workgroup's query rows (waves w and
+// w + NW own the same 32 rows) and take alternate KV tiles, each in its own
+// pair of LDS buffers; at the end the second group's dQ partial sums are added
+// to the first's through LDS, in a fixed order (small grids: twice the waves).
+template <typename T, int HD, int BC, int NW, int NG, bool CAUSAL, bool WINDOW, bool ALIBI>
+__global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const T* __restrict__ dO,
     const float* __restrict__ LSE, const float* __restrict__ Dd, T* __restrict__ dQ, Problem pb, float c,
     float scale, int nqt) {
   constexpr int BR = 32 * NW;
-  constexpr int NT = NW * 64;
+  constexpr int NT = NW * 64;  // threads of one group
+  static_assert(NG == 1 || NG == 2, "one or two wave groups");
   using Tile = RowTile<T, BC, HD>;
   constexpr int kOffK = 0;
   constexpr int kOffV = Tile::kElems;
   constexpr int kElems = 2 * Tile::kElems;
-  __shared__ __attribute__((aligned(16))) T lds[2 * kElems];
+  __shared__ __attribute__((aligned(16))) T lds[NG * 2 * kElems];  // [group][buf] K, V tiles
 
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
+  const int w = wv & (NW - 1);                              // the wave's 32 rows
+  const int grp = wv / NW;                                  // its group
+  const int gtid = tid & (NT - 1);                          // thread within the group
   const int lane = tid & 63, r = lane & 31, h = lane >> 5;
   const QTile wt = qtile_of<CAUSAL>(xcd_slice(blockIdx.x, gridDim.x), nqt, pb);
   const int b = wt.b, hq = wt.hq, qt = wt.qt;
@@ -468,13 +476,17 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   const int ntiles = hi > lo ? (hi + BC - 1) / BC - jt0 : 0;
 
   LoopLoader<T, BC, HD, NT> kld, vld;
-  kld.init(tid);
-  vld.init(tid);
-  if (ntiles > 0) {
-    kld.issue(Kh, jt0 * BC, sv.skv, lds + kOffK, tid);
-    vld.issue(Vh, jt0 * BC, sv.skv, lds + kOffV, tid);
-    kld.land(tid);
-    vld.land(tid);
+  kld.init(gtid);
+  vld.init(gtid);
+  // a group takes tiles grp, grp + NG, ... of the range, in its own buffers
+  T* const gl = lds + grp * 2 * kElems;
+  const int mine = ntiles > grp ? (ntiles - grp + NG - 1) / NG : 0;  // this group's tiles
+  const int steps = (ntiles + NG - 1) / NG;                        // every group's loop count
+  if (mine > 0) {
+    kld.issue(Kh, (jt0 + grp) * BC, sv.skv, gl + kOffK, gtid);
+    vld.issue(Vh, (jt0 + grp) * BC, sv.skv, gl + kOffV, gtid);
+    kld.land(gtid);
+    vld.land(gtid);
   }
   __syncthreads();
   // Everything issued so far has landed; a wait the compiler sees tells it
@@ -483,18 +495,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 
   // unrolled by two: every LDS address names its buffer at compile time
-  auto tile = [&](const int it, auto bufc) __attribute__((always_inline)) {
+  auto tile = [&](const int li, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
-    const int j0 = (jt0 + it) * BC;
-    const bool more = it + 1 < ntiles;
+    const int j0 = (jt0 + li * NG + grp) * BC;
+    const bool more = li + 1 < mine;
     if (more) {  // the other buffer was last read before the previous barrier
-      T* nb = lds + (buf ^ 1) * kElems;
-      kld.issue(Kh, j0 + BC, sv.skv, nb + kOffK, tid);
-      vld.issue(Vh, j0 + BC, sv.skv, nb + kOffV, tid);
+      T* nb = gl + (buf ^ 1) * kElems;
+      kld.issue(Kh, j0 + NG * BC, sv.skv, nb + kOffK, gtid);
+      vld.issue(Vh, j0 + NG * BC, sv.skv, nb + kOffV, gtid);
     }
-    const T* Ks = lds + buf * kElems + kOffK;
-    const T* Vs = lds + buf * kElems + kOffV;
-    const bool active = (!CAUSAL || j0 <= qw0 + 31 + off) &&
+    const T* Ks = gl + buf * kElems + kOffK;
+    const T* Vs = gl + buf * kElems + kOffV;
+    // (a group with one tile fewer sits out the last step)
+    const bool active = (NG == 1 || li < mine) && (!CAUSAL || j0 <= qw0 + 31 + off) &&
                         (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
     if (active) {
       const bool edge = (CAUSAL && j0 + BC - 1 > qw0 + off) ||
@@ -560,9 +573,33 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
     }
     __syncthreads();
   };
-  for (int it = 0; it < ntiles; it += 2) {
-    tile(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) tile(it + 1, std::integral_constant<int, 1>{});
+  for (int li = 0; li < steps; li += 2) {
+    tile(li, std::integral_constant<int, 0>{});
+    if (li + 1 < steps) tile(li + 1, std::integral_constant<int, 1>{});
+  }
+
+  if constexpr (NG == 2) {
+    // the second group's dQ partial sums through the (now free) tile buffers
+    static_assert(NW * (HD / 32) * 16 * 64 * 4 <= (int)sizeof(lds), "a group's accumulators fit the tile buffers");
+    f32x4* xf = reinterpret_cast<f32x4*>(lds);
+    if (grp == 1) {
+#pragma unroll
+      for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          xf[((w * (HD / 32) + d) * 4 + g) * 64 + lane] =
+              f32x4{acc[d][4 * g], acc[d][4 * g + 1], acc[d][4 * g + 2], acc[d][4 * g + 3]};
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 x = xf[((w * (HD / 32) + d) * 4 + g) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[d][4 * g + e] += x[e];
+      }
   }
 
   if (myq < sv.sq) {
@@ -577,14 +614,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dq_kernel(
 }
 
 // ------------------------------------------------------------------ launch
-template <typename T, int HD, int NW, bool CAUSAL, bool WINDOW, bool ALIBI>
+template <typename T, int HD, int NW, int NG, bool CAUSAL, bool WINDOW, bool ALIBI>
 static void launch_dq_nw(const BwdArgs& a, hipStream_t st, float c) {
   constexpr int BC = 64;
   const Problem& pb = a.pb;
   const int nqt = (pb.Sq + 32 * NW - 1) / (32 * NW);
   dim3 grid(nqt * pb.B * pb.Hq);
   if (grid.x > 0)
-    hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, CAUSAL, WINDOW, ALIBI>), grid, dim3(NW * 64), 0, st, (const T*)a.q,
+    hipLaunchKernelGGL((dq_kernel<T, HD, BC, NW, NG, CAUSAL, WINDOW, ALIBI>), grid, dim3(NG * NW * 64), 0, st, (const T*)a.q,
                        (const T*)a.k, (const T*)a.v, (const T*)a.dO, a.lse, (const float*)a.rowdot, (T*)a.dq, pb, c,
                        a.scale, nqt);
 }
@@ -644,9 +681,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   bool wide = false;
   if constexpr (sizeof(T) == 2) {  // fp32 keeps 4-wave workgroups (no 8-wave instances)
     wide = (long long)((pb.Sq + 255) / 256) * pb.B * pb.Hq >= kWideGrid;
-    if (wide) launch_dq_nw<T, HD, 8, CAUSAL, WINDOW, ALIBI>(a, st, c);
+    if (wide) launch_dq_nw<T, HD, 8, 1, CAUSAL, WINDOW, ALIBI>(a, st, c);
   }
-  if (!wide) launch_dq_nw<T, HD, 4, CAUSAL, WINDOW, ALIBI>(a, st, c);
+  if (!wide) {
+    // 16-bit grids of one 4-wave workgroup per CU or fewer: two wave groups
+    // per workgroup split the KV tiles (two waves per SIMD instead of one)
+    bool split = false;
+    if constexpr (sizeof(T) == 2) {
+      split = (long long)((pb.Sq + 127) / 128) * pb.B * pb.Hq <= kCUs;
+      if (split) launch_dq_nw<T, HD, 4, 2, CAUSAL, WINDOW, ALIBI>(a, st, c);
+    }
+    if (!split) launch_dq_nw<T, HD, 4, 1, CAUSAL, WINDOW, ALIBI>(a, st, c);
+  }
   mark(a.ev, a.nev, 3, st);
   return hipGetLastError();
 }
