@@ -126,9 +126,9 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
-  const int w = wv % NW;                                    // the wave's 32 keys
-  const int grp = wv / NW;                                  // its group
-  const int gtid = tid % NT;                                // thread index within the group
+  const int w = NG == 1 ? wv : wv % NW;                     // the wave's 32 keys
+  const int grp = NG == 1 ? 0 : wv / NW;                    // its group
+  const int gtid = NG == 1 ? tid : tid % NT;                // thread index within the group
   const int lane = tid & 63, r = lane & 31, h = lane >> 5;
   // work item: (b*Hkv + hkv) major, key tiles in order within a group (small
   // key tiles see the most queries: launched first); one XCD takes a
@@ -198,8 +198,8 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
   int cur_hq = hq0, cur_qt = nqt - 1;  // the tile in the group's LDS buffer `step & 1`
   if (grp == 1) advance(cur_hq, cur_qt);
   int nxt_hq = cur_hq, nxt_qt = cur_qt;  // the tile being prefetched
-  const int mine = total > grp ? (total - grp + NG - 1) / NG : 0;  // this group's iterations
-  const int steps = (total + NG - 1) / NG;                         // every group's loop count
+  const int mine = NG == 1 ? total : total > grp ? (total - grp + NG - 1) / NG : 0;  // this group's iterations
+  const int steps = NG == 1 ? total : (total + NG - 1) / NG;                       // every group's loop count
   // a head's first query row, from the group's first head (no offset loads)
   const size_t hstride = q_head_stride(pb);
   // L and D of the tile's rows: every lane loads one (lanes past BQ repeat a
@@ -433,9 +433,9 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index: uniform
-  const int w = wv & (NW - 1);                              // the wave's 32 rows
-  const int grp = wv / NW;                                  // its group
-  const int gtid = tid & (NT - 1);                          // thread within the group
+  const int w = NG == 1 ? wv : wv & (NW - 1);               // the wave's 32 rows
+  const int grp = NG == 1 ? 0 : wv / NW;                    // its group
+  const int gtid = NG == 1 ? tid : tid & (NT - 1);          // thread within the group
   const int lane = tid & 63, r = lane & 31, h = lane >> 5;
   const QTile wt = qtile_of<CAUSAL>(xcd_slice(blockIdx.x, gridDim.x), nqt, pb);
   const int b = wt.b, hq = wt.hq, qt = wt.qt;
@@ -479,12 +479,19 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
   kld.init(gtid);
   vld.init(gtid);
   // a group takes tiles grp, grp + NG, ... of the range, in its own buffers
-  T* const gl = lds + grp * 2 * kElems;
-  const int mine = ntiles > grp ? (ntiles - grp + NG - 1) / NG : 0;  // this group's tiles
-  const int steps = (ntiles + NG - 1) / NG;                        // every group's loop count
+  // (buffer bb of the group; formed from the array itself, which keeps the
+  // one-group kernel's LDS addressing as it was)
+  auto gbuf = [&](int bb) __attribute__((always_inline)) -> T* {
+    if constexpr (NG == 1)
+      return lds + bb * kElems;
+    else
+      return lds + (grp * 2 + bb) * kElems;
+  };
+  const int mine = NG == 1 ? ntiles : ntiles > grp ? (ntiles - grp + NG - 1) / NG : 0;  // this group's tiles
+  const int steps = NG == 1 ? ntiles : (ntiles + NG - 1) / NG;                         // every group's loop count
   if (mine > 0) {
-    kld.issue(Kh, (jt0 + grp) * BC, sv.skv, gl + kOffK, gtid);
-    vld.issue(Vh, (jt0 + grp) * BC, sv.skv, gl + kOffV, gtid);
+    kld.issue(Kh, (jt0 + grp) * BC, sv.skv, gbuf(0) + kOffK, gtid);
+    vld.issue(Vh, (jt0 + grp) * BC, sv.skv, gbuf(0) + kOffV, gtid);
     kld.land(gtid);
     vld.land(gtid);
   }
@@ -500,12 +507,12 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
     const int j0 = (jt0 + li * NG + grp) * BC;
     const bool more = li + 1 < mine;
     if (more) {  // the other buffer was last read before the previous barrier
-      T* nb = gl + (buf ^ 1) * kElems;
+      T* nb = gbuf(buf ^ 1);
       kld.issue(Kh, j0 + NG * BC, sv.skv, nb + kOffK, gtid);
       vld.issue(Vh, j0 + NG * BC, sv.skv, nb + kOffV, gtid);
     }
-    const T* Ks = gl + buf * kElems + kOffK;
-    const T* Vs = gl + buf * kElems + kOffV;
+    const T* Ks = gbuf(buf) + kOffK;
+    const T* Vs = gbuf(buf) + kOffV;
     // (a group with one tile fewer sits out the last step)
     const bool active = (NG == 1 || li < mine) && (!CAUSAL || j0 <= qw0 + 31 + off) &&
                         (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
@@ -685,9 +692,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   if (!wide) {
     // 16-bit grids of one 4-wave workgroup per CU or fewer: two wave groups
-    // per workgroup split the KV tiles (two waves per SIMD instead of one)
+    // per workgroup split the KV tiles (two waves per SIMD instead of one;
+    // ALiBi's extra registers do not fit it)
     bool split = false;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && !ALIBI) {
       split = (long long)((pb.Sq + 127) / 128) * pb.B * pb.Hq <= kCUs;
       if (split) launch_dq_nw<T, HD, 4, 2, CAUSAL, WINDOW, ALIBI>(a, st, c);
     }

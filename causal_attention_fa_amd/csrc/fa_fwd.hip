@@ -79,9 +79,9 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
   __shared__ __attribute__((aligned(16))) T lds[NG * 2 * kVOff];  // [group] K0, K1, V0, V1
 
   const int tid = threadIdx.x;
-  const int w = (tid >> 6) & (NW - 1), lane = tid & 63, r = lane & 31, h = lane >> 5;
+  const int w = NG == 1 ? tid >> 6 : (tid >> 6) & (NW - 1), lane = tid & 63, r = lane & 31, h = lane >> 5;
   const int grp = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / NW;  // the wave's group
-  const int gtid = tid & (NT - 1);                                                  // thread within it
+  const int gtid = NG == 1 ? tid : tid & (NT - 1);                                                  // thread within it
   // work item: KV group major, then query tile (heaviest first), then the
   // group's heads; one XCD takes a contiguous run of work items
   const QTile wt = qtile_of<CAUSAL>(xcd_slice(blockIdx.x, gridDim.x), nqt, pb);
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
   vld.init(gtid);
   // a group takes stages grp, grp + NG, ... of the tile's range, in its own buffers
   T* const gl = lds + grp * 2 * kVOff;
-  const int mine = nstages > grp ? (nstages - grp + NG - 1) / NG : 0;  // this group's stages
-  const int steps = (nstages + NG - 1) / NG;                         // every group's loop count
+  const int mine = NG == 1 ? nstages : nstages > grp ? (nstages - grp + NG - 1) / NG : 0;  // this group's stages
+  const int steps = NG == 1 ? nstages : (nstages + NG - 1) / NG;                          // every group's loop count
   if (mine > 0 && loader) {
     kld.issue(Kh, (jt0 + grp) * BS, sv.skv, gl, gtid);
     vld.issue(Vh, (jt0 + grp) * BS, sv.skv, gl + kVOff, gtid);
