@@ -25,6 +25,7 @@ from .dense import (  # noqa: F401
     sdpa_forward_rows,
     sdpa_backward,
     sdpa_dq_rows,
+    sdpa_dkdv_keys,
     softmax_probs,
     visible,
     sdpa_forward_varlen,

@@ -226,6 +226,33 @@ def sdpa_dq_rows(q, k, v, do, scale, causal, b, h, rows, window=None, alibi=None
     return scale * (dS @ kh[:nc])
 
 
+def sdpa_dkdv_keys(q, k, v, do, scale, causal, b, g, keys, window=None, alibi=None):
+    """dK and dV of selected keys of one (b, KV head g): ((n, D), (n, D)) in fp64.
+
+    A key's gradients are sums over the query rows that see it, of every query
+    head of the group (the chain rule through the GQA mapping), so only those
+    rows are formed: each one's full softmax row (its normalisation needs every
+    key it sees), its dP row and its D, as in ``sdpa_backward``."""
+    B, Hq, Hkv, Sq, Skv, D = _check_shapes(q, k, v)
+    off = Skv - Sq
+    G = Hq // Hkv
+    keys = np.asarray(keys, dtype=np.int64)
+    kh, vh = _f64(k[b, g]), _f64(v[b, g])
+    every = np.arange(Sq, dtype=np.int64)
+    rows = every[visible(every, keys, causal, off, window).any(axis=1)]
+    dk = np.zeros((keys.size, D))
+    dv = np.zeros((keys.size, D))
+    if rows.size == 0:
+        return dk, dv
+    for h in range(g * G, (g + 1) * G):
+        qr, dor = _f64(q[b, h][rows]), _f64(do[b, h][rows])
+        P, _, nc, _, dS = _row_block_backward(qr, rows, dor, kh, vh, scale, causal, off, window, _slope(alibi, h))
+        inside = keys < nc  # keys past the rows' last visible column get nothing
+        dk[inside] += scale * (dS[:, keys[inside]].T @ qr)
+        dv[inside] += P[:, keys[inside]].T @ dor
+    return dk, dv
+
+
 def _seq_slices(cu):
     cu = np.asarray(cu, dtype=np.int64)
     return [(int(cu[i]), int(cu[i + 1])) for i in range(len(cu) - 1)]

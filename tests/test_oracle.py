@@ -598,6 +598,23 @@ def test_alibi_zero_keys_geometric_weights(Sq, Skv, causal):
             np.testing.assert_allclose(Lt[0, h, i], math.log(z), rtol=1e-13, atol=1e-13)
 
 
+@pytest.mark.parametrize("Sq,Skv,causal,window", MASK_CASES)
+def test_dkdv_keys_against_torch_fp64(Sq, Skv, causal, window):
+    """dK, dV of chosen keys (each summed over the rows that see it) against PyTorch's
+    fp64 gradients of the masked attention."""
+    r = np.random.default_rng(Sq * 7 + Skv)
+    q = r.standard_normal((2, 4, Sq, 8)) * 1.5
+    k, v = r.standard_normal((2, 2, Skv, 8)), r.standard_normal((2, 2, Skv, 8))
+    do = r.standard_normal((2, 4, Sq, 8))
+    vis, _, _, dk, dv = _torch_masked(q, k, v, do, 0.4, causal, window)
+    do0 = np.where(vis.any(axis=1)[None, None, :, None], do, 0.0)
+    keys = np.unique(np.concatenate([[0, Skv - 1], r.integers(0, Skv, 4)]))
+    for b, g in ((0, 0), (1, 1)):
+        gk, gv = oracle.sdpa_dkdv_keys(q, k, v, do0, 0.4, causal, b, g, keys, window=window)
+        np.testing.assert_allclose(gk, dk[b, g, keys], atol=1e-12)
+        np.testing.assert_allclose(gv, dv[b, g, keys], atol=1e-12)
+
+
 def _torch_alibi(q, k, v, do, scale, causal, window, slopes):
     """PyTorch's fp64 SDPA with the bias passed as an additive float mask (-inf where hidden)."""
     B, Hq, Sq, D = q.shape
@@ -620,6 +637,19 @@ def _torch_alibi(q, k, v, do, scale, causal, window, slopes):
 
 
 ALIBI_CASES = [(19, 19, True, None), (19, 19, False, None), (11, 23, True, 5), (23, 11, False, 3), (16, 16, True, 0)]
+
+
+def test_dkdv_keys_alibi_against_torch_fp64():
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((2, 4, 21, 8)) * 1.5
+    k, v = rng.standard_normal((2, 2, 21, 8)), rng.standard_normal((2, 2, 21, 8))
+    do = rng.standard_normal((2, 4, 21, 8))
+    ref = _torch_alibi(q, k, v, do, 0.35, True, None, SLOPES4)
+    keys = np.array([0, 3, 10, 20])
+    for b, g in ((0, 1), (1, 0)):
+        gk, gv = oracle.sdpa_dkdv_keys(q, k, v, do, 0.35, True, b, g, keys, alibi=SLOPES4)
+        np.testing.assert_allclose(gk, ref["dk"][b, g, keys], atol=1e-12, rtol=1e-10)
+        np.testing.assert_allclose(gv, ref["dv"][b, g, keys], atol=1e-12, rtol=1e-10)
 
 
 @pytest.mark.parametrize("Sq,Skv,causal,window", ALIBI_CASES)

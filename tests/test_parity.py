@@ -165,7 +165,8 @@ def test_workload_fp16_s4096():
 
 
 def test_workload_long_context_gqa_bf16():
-    """S = 16384: one whole KV group (4 query heads, every row) fwd + bwd, plus sampled rows of every head."""
+    """S = 16384: one whole KV group (4 query heads, every row) fwd + bwd, plus sampled rows of every
+    head (O, L, dQ) and the last keys of every KV group (dK, dV)."""
     w = WORKLOADS["longctx_gqa_causal_bf16_b1_h32kv8_s16384_d128"]
     inp = workload_inputs(w)
     say(f"workload {w.name}")
@@ -195,6 +196,16 @@ def test_workload_long_context_gqa_bf16():
     e = rel_l2(np.stack(dq_got), np.stack(dq_ref))
     assert e <= TOL[w.dtype]["grad"]
     say(f"  sampled rows of all heads: O max-abs {worst_o:.3e}, L {worst_l:.3e}, dq rel-L2 {e:.3e}")
+    # dK, dV of the last keys of every KV group (seen by the last rows only, so the
+    # oracle forms 256 rows per head): the groups the whole-group check leaves out
+    keys = np.unique(np.concatenate([np.arange(w.S - 32, w.S), rng.integers(w.S - 256, w.S, 8)]))
+    dkg, dkr, dvg, dvr = [], [], [], []
+    for g2 in range(w.Hkv):
+        rk, rv = oracle.sdpa_dkdv_keys(inp["q"], inp["k"], inp["v"], inp["do"], w.scale, True, 0, g2, keys)
+        dkg.append(got[1][0, g2, keys]), dkr.append(rk), dvg.append(got[2][0, g2, keys]), dvr.append(rv)
+    ek, ev = rel_l2(np.stack(dkg), np.stack(dkr)), rel_l2(np.stack(dvg), np.stack(dvr))
+    assert ek <= TOL[w.dtype]["grad"] and ev <= TOL[w.dtype]["grad"], (ek, ev)
+    say(f"  last keys of all KV groups: dk rel-L2 {ek:.3e}, dv rel-L2 {ev:.3e}")
 
 
 # ------------------------------------------------------------------ closed forms and edge cases
