@@ -397,7 +397,16 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     if (grp != 0) return;
   }
 
-  if (mykv < sv0.skv) {
+  if constexpr (sizeof(T) == 2 && !WINDOW && !ALIBI) {
+    // dK and dV rows leave through LDS, the wave's share of the V rows (read
+    // for the last time before the loop's last barrier): whole rows per store
+    // instruction.  The window and bias kernels store straight from the
+    // accumulators: they have no registers to spare for it.
+    static_assert(NW * 32 * HD <= VTile::kElems, "a wave's rows fit its share of the V rows");
+    T* stg = lds_v + w * 32 * HD;
+    store_block_rows<T, HD>(dk, scale, stg, dK + (sv0.kv_row0 + kw0) * HD, sv0.skv - kw0, lane);
+    store_block_rows<T, HD>(dv, 1.f, stg, dV + (sv0.kv_row0 + kw0) * HD, sv0.skv - kw0, lane);
+  } else if (mykv < sv0.skv) {
     T* dKr = dK + (sv0.kv_row0 + mykv) * HD;
     T* dVr = dV + (sv0.kv_row0 + mykv) * HD;
 #pragma unroll
@@ -571,6 +580,16 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
           for (int d = 0; d < HD / 32; ++d)
             acc[d] = mma<T>(Tile::tr_frag(Ks, 2 * kb + kk, 32 * d, lane), sf, acc[d]);
         }
+        if constexpr (sizeof(T) == 2) {
+          // the transposed K fragments of product n + 1 are read before product n
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+#pragma unroll
+          for (int n = 0; n < 2 * (HD / 32) - 1; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix products
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -609,7 +628,14 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
       }
   }
 
-  if (myq < sv.sq) {
+  if constexpr (sizeof(T) == 2 && !WINDOW && !ALIBI) {
+    // dQ rows leave through LDS (free after the loop's last barrier; with two
+    // groups, past the partial sums): whole rows per store instruction.  The
+    // window and bias kernels store straight from the accumulators.
+    constexpr int kStg = NG == 1 ? 0 : NW * (HD / 32) * 4 * 64 * 16 / (int)sizeof(T);
+    static_assert(kStg + NW * 32 * HD <= (int)(sizeof(lds) / sizeof(T)), "the dQ rows fit the tile buffers");
+    store_block_rows<T, HD>(acc, scale, lds + kStg + w * 32 * HD, dQ + (sv.q_row0 + qw0) * HD, sv.sq - qw0, lane);
+  } else if (myq < sv.sq) {
     T* dQr = dQ + (sv.q_row0 + myq) * HD;
 #pragma unroll
     for (int d = 0; d < HD / 32; ++d)

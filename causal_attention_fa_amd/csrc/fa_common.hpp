@@ -452,4 +452,40 @@ __device__ inline void store4(T* p, float a, float b, float c, float d) {
   *reinterpret_cast<vec4<T>*>(p) = v;
 }
 
+// Writes a wave's 32 x HD output block, held as 32x32 accumulators (lane
+// 32h + r: row r, columns 32d + 8g + 4h .. + 3 in acc[d][4g .. 4g + 3]), times
+// the lane's factor `mul`, to rows out[0 .. valid) (row stride HD) through a
+// private LDS region of 32 * HD elements.  Stored straight from the
+// accumulators, every store instruction would write 8 bytes in each of 32
+// rows; through LDS each writes whole rows, 16 bytes per lane.  The region is
+// laid out as a swizzled row tile, so the 32 rows of one column group fall in
+// different banks.  16-bit types only; the wave must be the region's only user.
+template <typename T, int HD>
+__device__ inline void store_block_rows(const f32x16 (&acc)[HD / 32], float mul, T* stg, T* out, int valid,
+                                        int lane) {
+  static_assert(sizeof(T) == 2, "16-bit outputs");
+  using Blk = RowTile<T, 32, HD>;
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int d = 0; d < HD / 32; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      store4<T>(stg + Blk::at(r, 32 * d + 8 * g + 4 * h), acc[d][4 * g] * mul, acc[d][4 * g + 1] * mul,
+                acc[d][4 * g + 2] * mul, acc[d][4 * g + 3] * mul);
+  // the wave reads back what its other lanes wrote: its LDS accesses complete
+  // in program order, and the fences keep the compiler from moving them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kLanesPerRow = HD * (int)sizeof(T) / 16;
+  constexpr int kRowsPerPass = 64 / kLanesPerRow;
+  const int pr = lane / kLanesPerRow, pc = (lane % kLanesPerRow) * 8;
+#pragma unroll
+  for (int i = 0; i < 32 / kRowsPerPass; ++i) {
+    const int row = pr + kRowsPerPass * i;
+    const vec8<T> x = load8<T>(stg + Blk::at(row, pc));
+    if (row < valid) *reinterpret_cast<vec8<T>*>(out + (size_t)row * HD + pc) = x;
+  }
+}
+
 }  // namespace fa

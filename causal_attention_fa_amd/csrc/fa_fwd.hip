@@ -299,9 +299,18 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
   }
 
   const float l = wave_xor32_sum(lsum);
-  if (myq < sv.sq) {
-    // a row that saw no key has an empty softmax: O = 0, L = -inf
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+  // a row that saw no key has an empty softmax: O = 0, L = -inf
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if constexpr (sizeof(T) == 2 && !WINDOW && !ALIBI) {
+    // O rows leave through LDS, free once every wave has passed the last
+    // stage's barrier (with two groups: past the merge state).  The window and
+    // bias kernels store straight from the accumulators: they have no
+    // registers to spare for it.
+    constexpr int kStg = NG == 1 ? 0 : NW * (HD / 32 * 4 + 1) * 64 * 16 / (int)sizeof(T);
+    static_assert(kStg + NW * 32 * HD <= (int)(sizeof(lds) / sizeof(T)), "the output rows fit the stage buffers");
+    store_block_rows<T, HD>(oacc, inv, lds + kStg + w * 32 * HD, O + (sv.q_row0 + qw0) * HD, sv.sq - qw0, lane);
+    if (LSE != nullptr && h == 0 && myq < sv.sq) LSE[sv.q_row0 + myq] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  } else if (myq < sv.sq) {
     T* Or = O + (sv.q_row0 + myq) * HD;
 #pragma unroll
     for (int d = 0; d < HD / 32; ++d)
