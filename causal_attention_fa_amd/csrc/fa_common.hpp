@@ -150,6 +150,16 @@ __device__ inline float frag_sum(const vec8<float>& f, float acc) {
   return acc + (((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7])));
 }
 
+// acc += sel * p as a 16x16x32 product (16-bit operands, fp32 accumulation):
+// the row sums of fwd_kernel's rounded P, with its constant 0/1 selector.
+template <typename T>
+__device__ inline f32x4 row_sum_mma(const vec8<T>& sel, const vec8<T>& p, f32x4 acc) {
+  if constexpr (std::is_same<T, __bf16>::value)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p, acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, p, acc, 0, 0, 0);
+}
+
 // Workgroup order for MI355X's 8 XCDs.  The dispatcher hands consecutive
 // workgroup ids to the XCDs round-robin (id % 8), and each XCD has its own L2.
 // Returns the work item a workgroup should take so that XCD x processes the

@@ -109,10 +109,24 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
   f32x16 oacc[HD / 32];
 #pragma unroll
   for (int d = 0; d < HD / 32; ++d) oacc[d] = f32x16{};
-  // Row sum of the rounded P that multiplies V: each lane sums its half of
-  // the tile's keys (packed dot products on the vector ALU, which has slack
-  // beside the matrix cores); the two halves are added at the end.
+  // Row sum of the rounded P that multiplies V.  16-bit: on the matrix core,
+  // one 16x16x32 product per 16 keys with a constant 0/1 operand: read as
+  // that product's B operand, a lane pair's P fragment gives output row 0
+  // the keys of query n and row 1 those of query n + 16 (n = lane % 16), so
+  // lanes 0-15 accumulate every row's sum in rsum[0] and rsum[1].  (Packed
+  // dot products on the vector ALU, the fp32 form, wait for the matrix core
+  // when they run beside its products.)  fp32: each lane sums its half of
+  // the keys and the halves are added at the end.
+  constexpr bool kRowSumMfma = sizeof(T) == 2;
   float lsum = 0.f;
+  f32x4 rsum = {0.f, 0.f, 0.f, 0.f};
+  vec8<T> sel;
+  {
+    const int n = lane & 15, j = (lane >> 4) & 1;
+    const T v = (T)(((n == 0 && j == 0) || (n == 1 && j == 1)) ? 1.f : 0.f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[e] = v;
+  }
   float m = -INFINITY;
 
   // keys the workgroup's rows can see: [lo, hi)
@@ -234,6 +248,12 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
           // a row that has seen no key keeps m = -inf and alpha = 1
           const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
           lsum *= alpha;
+          if constexpr (kRowSumMfma) {
+            // rsum[1] of lane n holds query n + 16's sum: its factor is lane n + 16's
+            const float a16 = __shfl_xor(alpha, 16);
+            rsum[0] *= alpha;
+            rsum[1] *= a16;
+          }
 #pragma unroll
           for (int d = 0; d < HD / 32; ++d) oacc[d] *= alpha;
           m = m_new;
@@ -249,7 +269,10 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
           const vec8<T> pf = acc_to_frag<T>(s[kt >> 1], 8 * (kt & 1));
 #pragma unroll
           for (int d = 0; d < HD / 32; ++d) oacc[d] = mma<T>(Tile::tr_frag(Vs, kt, 32 * d, lane), pf, oacc[d]);
-          lsum = frag_sum(pf, lsum);
+          if constexpr (kRowSumMfma)
+            rsum = row_sum_mma<T>(sel, pf, rsum);
+          else
+            lsum = frag_sum(pf, lsum);
         }
       }
     }
@@ -264,6 +287,13 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
     if (li + 1 < steps) stage(li + 1, gl + Stage::kElems, gl);
   }
 
+  if constexpr (kRowSumMfma) {
+    // every lane of a row pair takes its query's whole sum (the merge below is
+    // linear in it)
+    const int src = r & 15;
+    const float s0 = __shfl(rsum[0], src), s1 = __shfl(rsum[1], src);
+    lsum = r < 16 ? s0 : s1;
+  }
   if constexpr (NG == 2) {
     // the second group's reference, lane sum and accumulators, through the
     // (now free) stage buffers; the first group rescales both to the larger
@@ -298,7 +328,7 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
     m = mm;
   }
 
-  const float l = wave_xor32_sum(lsum);
+  const float l = kRowSumMfma ? lsum : wave_xor32_sum(lsum);
   // a row that saw no key has an empty softmax: O = 0, L = -inf
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if constexpr (sizeof(T) == 2 && !WINDOW && !ALIBI) {
