@@ -382,7 +382,7 @@ def _time_each(fn, n, warmup, stream, hip):
     return out
 
 
-def config_table(skip, steps, warmup):
+def config_table(skip):
     """Forward and backward of every workload, each timed call by call on resident
     inputs: median / min / mean ms, TFLOP/s at the median and % of the dtype's
     matrix peak (bf16 / fp16 2516.6, fp32 157.3 TFLOP/s)."""
@@ -413,10 +413,12 @@ def config_table(skip, steps, warmup):
             if st != fa.FA_OK:
                 raise fa.FAError(st, "fa_fwd")
 
-        n = 100 if w.fwd_flops() < 1e11 else steps
+        # 200 calls after at least 50 warm-ups: long enough for the clock to settle
+        # (every workload here runs 0.02-0.2 ms per call)
+        n, warm = 200, 50
         row = {"workload": w.name, "dtype": w.dtype, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "S": w.S, "D": w.D,
                "peak_tflops": peak}
-        ms = _time_each(fwd, n, warmup, sh, hip)
+        ms = _time_each(fwd, n, warm, sh, hip)
         row["fwd"] = dict(stats(ms), calls=n)
         tf = w.fwd_flops() / (statistics.median(ms) * 1e-3) / 1e12
         row["fwd"].update(tflops=round(tf, 2), pct_of_peak=round(100 * tf / peak, 2))
@@ -434,7 +436,7 @@ def config_table(skip, steps, warmup):
                 if st != fa.FA_OK:
                     raise fa.FAError(st, "fa_bwd")
 
-            ms = _time_each(bwd, n, warmup, sh, hip)
+            ms = _time_each(bwd, n, warm, sh, hip)
             row["bwd"] = dict(stats(ms), calls=n)
             tf = w.bwd_flops() / (statistics.median(ms) * 1e-3) / 1e12
             row["bwd"].update(tflops=round(tf, 2), pct_of_peak=round(100 * tf / peak, 2))
@@ -731,7 +733,7 @@ def main():
             "note": "256 CUs x the sampled graphics clock under that work x 4096 bf16 flop/clk/CU; the 2516.6 "
                     f"TFLOP/s peak assumes {clock['forward'].get('max_clk_mhz')} MHz"}
     if not args.no_configs:
-        out["configs"] = config_table({w.name}, 20, 5)
+        out["configs"] = config_table({w.name})
     if not args.no_sweep:
         out["forward_sweep"] = forward_sweep(10, 3, args.sweep_ms)
     if not args.no_decode:
