@@ -535,20 +535,34 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
         // dP^T starts from -D of the lane's row, so dS = P (dP - D) is one
         // multiply per element
         f32x16 s, dp;
-#pragma unroll
-        for (int t = 0; t < HD / 16; ++t) {
-          s = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], t == 0 ? f32x16{} : s);
-          dp = mma<T>(Tile::frag(Vs, 32 * kb + r, 16 * t, h), df[t], t == 0 ? ndq : dp);
-        }
         if constexpr (sizeof(T) == 2) {
-          // the K and V fragments of step t+1 are read before the products of step t
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+          // the K and V fragments of step t+2 are read before the products of
+          // step t, in registers of their own, and a fence after every step
+          // keeps the S and dP products alternating (with a scheduling hint
+          // alone the compiler ran the whole S chain first, each product
+          // waiting for the fragment read just before it)
+          constexpr int NS = HD / 16;
+          vec8<T> kq[NS], vq[NS];
+          kq[0] = Tile::frag(Ks, 32 * kb + r, 0, h);
+          vq[0] = Tile::frag(Vs, 32 * kb + r, 0, h);
+          kq[1] = Tile::frag(Ks, 32 * kb + r, 16, h);
+          vq[1] = Tile::frag(Vs, 32 * kb + r, 16, h);
 #pragma unroll
-          for (int t = 0; t < HD / 16 - 1; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // matrix products
+          for (int t = 0; t < NS; ++t) {
+            if (t + 2 < NS) {
+              kq[t + 2] = Tile::frag(Ks, 32 * kb + r, 16 * (t + 2), h);
+              vq[t + 2] = Tile::frag(Vs, 32 * kb + r, 16 * (t + 2), h);
+            }
+            s = mma<T>(kq[t], qf[t], t == 0 ? f32x16{} : s);
+            dp = mma<T>(vq[t], df[t], t == 0 ? ndq : dp);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        } else {
+#pragma unroll
+          for (int t = 0; t < HD / 16; ++t) {
+            s = mma<T>(Tile::frag(Ks, 32 * kb + r, 16 * t, h), qf[t], t == 0 ? f32x16{} : s);
+            dp = mma<T>(Tile::frag(Vs, 32 * kb + r, 16 * t, h), df[t], t == 0 ? ndq : dp);
+          }
         }
         // P and dS; the masked form is a branch of its own (a mask inside the
         // loop is computed, and selected, for every tile)
