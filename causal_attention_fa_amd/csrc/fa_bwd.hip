@@ -259,21 +259,35 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) nd[4 * g4 + e] = x[e];
         }
-#pragma unroll
-        for (int t = 0; t < HD / 16; ++t) {
-          s[qb] = mma<T>(Tile::frag(Qs, 32 * qb + r, 16 * t, h), kf[t], t == 0 ? f32x16{} : s[qb]);
-          dp[qb] = mma<T>(Tile::frag(dOs, 32 * qb + r, 16 * t, h), VTile::frag(lds_v, 32 * w + r, 16 * t, h),
-                          t == 0 ? nd : dp[qb]);
-        }
         if constexpr (sizeof(T) == 2) {
-          // the Q, dO and V fragments of step t+1 are read before the products of step t
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads
+          // the Q, dO and V fragments of step t + LA are read before the
+          // products of step t, in registers of their own, and a fence after
+          // every step keeps the S and dP products alternating; the read-ahead
+          // variant (one wave per SIMD) has the registers for two steps
+          constexpr int NS = HD / 16;
+          constexpr int LA = AHEAD ? 2 : 1;
+          vec8<T> qq[NS], oq[NS], vq[NS];
+          auto rd = [&](int t) __attribute__((always_inline)) {
+            qq[t] = Tile::frag(Qs, 32 * qb + r, 16 * t, h);
+            oq[t] = Tile::frag(dOs, 32 * qb + r, 16 * t, h);
+            vq[t] = VTile::frag(lds_v, 32 * w + r, 16 * t, h);
+          };
+          rd(0);
+          if constexpr (LA == 2) rd(1);
 #pragma unroll
-          for (int t = 0; t < HD / 16 - 1; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // matrix products
+          for (int t = 0; t < NS; ++t) {
+            if (t + LA < NS) rd(t + LA);
+            s[qb] = mma<T>(qq[t], kf[t], t == 0 ? f32x16{} : s[qb]);
+            dp[qb] = mma<T>(oq[t], vq[t], t == 0 ? nd : dp[qb]);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        } else {
+#pragma unroll
+          for (int t = 0; t < HD / 16; ++t) {
+            s[qb] = mma<T>(Tile::frag(Qs, 32 * qb + r, 16 * t, h), kf[t], t == 0 ? f32x16{} : s[qb]);
+            dp[qb] = mma<T>(Tile::frag(dOs, 32 * qb + r, 16 * t, h), VTile::frag(lds_v, 32 * w + r, 16 * t, h),
+                            t == 0 ? nd : dp[qb]);
+          }
         }
       }
       // invisible (query, key) pairs and queries past the end get p = 0 (keys
