@@ -274,6 +274,19 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
           else
             lsum = frag_sum(pf, lsum);
         }
+        if constexpr (kRowSumMfma) {
+          // the transposed V reads of 16-key step kt+1 before the four PV
+          // products and the row-sum product of step kt (left to itself, the
+          // compiler put a stage's row-sum products at its end, one dependent
+          // chain, holding every P fragment of the stage until then)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (HD / 32), 0);  // LDS reads
+#pragma unroll
+          for (int kt = 0; kt < BC / 16 - 1; ++kt) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (HD / 32), 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, HD / 32 + 1, 0);  // matrix products
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, HD / 32 + 1, 0);
+        }
       }
     }
     if (more && loader) {
