@@ -275,3 +275,34 @@ def test_wide_grid_masks(causal, window, S, Skv, D, dtype):
     heads = list(range(5 * 4, 6 * 4))
     check_o(o[3, heads], g["o"][3, heads], dtype, what + " group")
     check_grads((dq[3, heads], dk[3, 5], dv[3, 5]), (g["dq"][3, heads], g["dk"][3, 5], g["dv"][3, 5]), dtype, what)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("causal,window,S", [(True, None, 2048), (True, None, 1999), (False, 600, 2048)])
+def test_read_ahead_dkdv_grid(causal, window, S, dtype):
+    """B = 4, 32/8 heads, D = 128: ceil(S/128) * 4 * 8 = 512 four-wave key blocks, more
+    than one and at most three per CU, which dispatches the dK/dV kernel's one-wave-per-SIMD
+    form that reads its fragments ahead (and, with 8-wave query blocks from 256, the
+    8-wave forward).  One whole KV group's O and gradients against the oracle, and
+    sampled rows of the gradients of every other KV head (and the last)."""
+    B, Hq, Hkv, D = 4, 32, 8, 128
+    scale = 1.0 / math.sqrt(D)
+    inp = make_inputs(B, Hq, Hkv, S, D, dtype, seed=4700 + S + (window or 0), q_std=2.0)
+    what = f"read-ahead dK/dV grid {dtype} causal={causal} window={window} S={S}"
+    say("case", what)
+    o, lse, (dq, dk, dv) = run_dense(inp, dtype, scale, causal, window)
+    b, g = 2, 6
+    ref = oracle.sdpa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, groups=[(b, g)], window=window)
+    heads = list(range(g * 4, (g + 1) * 4))
+    check_o(o[b, heads], ref["o"][b, heads], dtype, what + " group")
+    check_grads((dq[b, heads], dk[b, g], dv[b, g]), (ref["dq"][b, heads], ref["dk"][b, g], ref["dv"][b, g]),
+                dtype, what)
+    rows = np.array([0, 1, 31, 32, 255, 256, S // 2, S - 2, S - 1])
+    for bb in (0, 3):
+        for kh in (0, 2, 4, 7):
+            r = oracle.sdpa_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, groups=[(bb, kh)],
+                                     window=window)
+            check_grads((dq[bb, kh * 4:(kh + 1) * 4, rows], dk[bb, kh, rows], dv[bb, kh, rows]),
+                        (r["dq"][bb, kh * 4:(kh + 1) * 4, rows], r["dk"][bb, kh, rows], r["dv"][bb, kh, rows]),
+                        dtype, f"{what} b={bb} kv={kh}")
