@@ -113,10 +113,10 @@ __global__ __launch_bounds__(NG * NW * 64, (sizeof(T) == 2 ? 2 : 1)) void fwd_ke
   // one 16x16x32 product per 16 keys with a constant 0/1 operand: read as
   // that product's B operand, a lane pair's P fragment gives output row 0
   // the keys of query n and row 1 those of query n + 16 (n = lane % 16), so
-  // lanes 0-15 accumulate every row's sum in rsum[0] and rsum[1].  (Packed
-  // dot products on the vector ALU, the fp32 form, wait for the matrix core
-  // when they run beside its products.)  fp32: each lane sums its half of
-  // the keys and the halves are added at the end.
+  // lanes 0-15 accumulate every row's sum in rsum[0] and rsum[1].  (Summed
+  // instead with packed dot products on the vector ALU, the 16-bit pairs wait
+  // for the matrix core while its products run.)  fp32: each lane sums its
+  // half of the keys on the vector ALU and the halves are added at the end.
   constexpr bool kRowSumMfma = sizeof(T) == 2;
   float lsum = 0.f;
   f32x4 rsum = {0.f, 0.f, 0.f, 0.f};
