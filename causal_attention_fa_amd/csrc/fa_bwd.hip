@@ -168,6 +168,25 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     dk[d] = f32x16{};
     dv[d] = f32x16{};
   }
+  // byte offsets of the lane's fragment reads (16-bit tiles), computed once
+  // and kept in registers so a read's tile and step parts are its immediate:
+  // fro: row r, columns 16t + 8h of a 32-row Q / dO block; vro: the same in
+  // this wave's V rows; tro: the two transposed reads for dK / dV columns 32d
+  uint32_t fro[HD / 16], vro[HD / 16], tro[HD / 32][2];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int t = 0; t < HD / 16; ++t) {
+      fro[t] = (uint32_t)(Tile::at(r, 16 * t + 8 * h) * (int)sizeof(T));
+      vro[t] = (uint32_t)(VTile::at(32 * w + r, 16 * t + 8 * h) * (int)sizeof(T));
+    }
+    const int x = 4 * (lane >> 5) + ((lane & 15) >> 2);
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d) {
+      const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      tro[d][0] = (uint32_t)(Tile::at(x, col) * (int)sizeof(T));
+      tro[d][1] = (uint32_t)(Tile::at(x + 8, col) * (int)sizeof(T));
+    }
+  }
 
   // query rows that can see one of the keys [kv0, kv0 + BKV): [qlo, qhi)
   const int qlo = CAUSAL ? max(0, kv0 - off) : 0;
@@ -228,8 +247,9 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     commit(0);
   }
   __syncthreads();
-  for (int it = 0; it < steps; ++it) {
-    const int buf = it & 1;
+  // unrolled by two: every LDS address names its buffer at compile time
+  auto body = [&](const int it, auto bufc) __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     const int i0 = cur_qt * BQ;
     const bool more = it + 1 < mine;
     if (more) {  // the other buffer was last read before the previous barrier
@@ -239,6 +259,15 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     }
     const T* Qs = lds + (grp * 2 + buf) * kElems + kOffQ;
     const T* dOs = lds + (grp * 2 + buf) * kElems + kOffD;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int t = 0; t < HD / 16; ++t) asm volatile("" : "+v"(fro[t]), "+v"(vro[t]));
+#pragma unroll
+      for (int d = 0; d < HD / 32; ++d) asm volatile("" : "+v"(tro[d][0]), "+v"(tro[d][1]));
+    }
+    auto at_b = [](const T* base, uint32_t b) __attribute__((always_inline)) {
+      return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + b);
+    };
     // does a query of the tile see one of this wave's keys?  (a group with
     // one iteration fewer sits out the last step)
     const bool active = it < mine && (!CAUSAL || i0 + BQ - 1 + off >= kw0) &&
@@ -268,9 +297,9 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
           constexpr int LA = AHEAD ? 2 : 1;
           vec8<T> qq[NS], oq[NS], vq[NS];
           auto rd = [&](int t) __attribute__((always_inline)) {
-            qq[t] = Tile::frag(Qs, 32 * qb + r, 16 * t, h);
-            oq[t] = Tile::frag(dOs, 32 * qb + r, 16 * t, h);
-            vq[t] = VTile::frag(lds_v, 32 * w + r, 16 * t, h);
+            qq[t] = load8<T>(at_b(Qs + 32 * qb * Tile::kStride, fro[t]));
+            oq[t] = load8<T>(at_b(dOs + 32 * qb * Tile::kStride, fro[t]));
+            vq[t] = load8<T>(at_b(lds_v, vro[t]));
           };
           rd(0);
           if constexpr (LA == 2) rd(1);
@@ -356,8 +385,18 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
         const vec8<T> sf = acc_to_frag<T>(dp[kt >> 1], 8 * (kt & 1));
 #pragma unroll
         for (int d = 0; d < HD / 32; ++d) {
-          dv[d] = mma<T>(Tile::tr_frag(dOs, kt, 32 * d, lane), pf, dv[d]);
-          dk[d] = mma<T>(Tile::tr_frag(Qs, kt, 32 * d, lane), sf, dk[d]);
+          if constexpr (sizeof(T) == 2) {
+            auto trp = [&](const T* tile) __attribute__((always_inline)) {
+              const T* tb = tile + 16 * kt * Tile::kStride;
+              const vec4<T> a4 = lds_tr4<T>(at_b(tb, tro[d][0])), b4 = lds_tr4<T>(at_b(tb, tro[d][1]));
+              return vec8<T>{a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]};
+            };
+            dv[d] = mma<T>(trp(dOs), pf, dv[d]);
+            dk[d] = mma<T>(trp(Qs), sf, dk[d]);
+          } else {
+            dv[d] = mma<T>(Tile::tr_frag(dOs, kt, 32 * d, lane), pf, dv[d]);
+            dk[d] = mma<T>(Tile::tr_frag(Qs, kt, 32 * d, lane), sf, dk[d]);
+          }
         }
       }
       if constexpr (AHEAD && sizeof(T) == 2) {
@@ -376,6 +415,10 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
 #pragma unroll
     for (int k = 0; k < NG; ++k) advance(cur_hq, cur_qt);
     __syncthreads();
+  };
+  for (int it = 0; it < steps; it += 2) {
+    body(it, std::integral_constant<int, 0>{});
+    if (it + 1 < steps) body(it + 1, std::integral_constant<int, 1>{});
   }
 
   if constexpr (NG == 2) {
@@ -491,6 +534,19 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
   f32x16 acc[HD / 32];
 #pragma unroll
   for (int d = 0; d < HD / 32; ++d) acc[d] = f32x16{};
+  // byte offsets within a K tile of the lane's two transposed reads for each
+  // 32-column block of dQ (16-bit tiles): computed once and kept in registers,
+  // so the tile and key-block parts of an address are the read's immediate
+  uint32_t tro[HD / 32][2];
+  if constexpr (sizeof(T) == 2) {
+    const int x = 4 * (lane >> 5) + ((lane & 15) >> 2);
+#pragma unroll
+    for (int d = 0; d < HD / 32; ++d) {
+      const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      tro[d][0] = (uint32_t)(Tile::at(x, col) * (int)sizeof(T));
+      tro[d][1] = (uint32_t)(Tile::at(x + 8, col) * (int)sizeof(T));
+    }
+  }
 
   const int last = min(i0 + BR, sv.sq) - 1;
   const int hi = CAUSAL ? min(sv.skv, last + off + 1) : sv.skv;
@@ -536,6 +592,10 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
     }
     const T* Ks = gbuf(buf) + kOffK;
     const T* Vs = gbuf(buf) + kOffV;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int d = 0; d < HD / 32; ++d) asm volatile("" : "+v"(tro[d][0]), "+v"(tro[d][1]));
+    }
     // (a group with one tile fewer sits out the last step)
     const bool active = (NG == 1 || li < mine) && (!CAUSAL || j0 <= qw0 + 31 + off) &&
                         (!WINDOW || j0 + BC - 1 >= qw0 + off - pb.window);
@@ -605,8 +665,17 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dq_kernel(
         for (int kk = 0; kk < 2; ++kk) {
           const vec8<T> sf = acc_to_frag<T>(dp, 8 * kk);
 #pragma unroll
-          for (int d = 0; d < HD / 32; ++d)
-            acc[d] = mma<T>(Tile::tr_frag(Ks, 2 * kb + kk, 32 * d, lane), sf, acc[d]);
+          for (int d = 0; d < HD / 32; ++d) {
+            if constexpr (sizeof(T) == 2) {
+              const char* tb = reinterpret_cast<const char*>(Ks + 16 * (2 * kb + kk) * Tile::kStride);
+              const vec4<T> lo4 = lds_tr4<T>(reinterpret_cast<const T*>(tb + tro[d][0]));
+              const vec4<T> hi4 = lds_tr4<T>(reinterpret_cast<const T*>(tb + tro[d][1]));
+              const vec8<T> kf = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+              acc[d] = mma<T>(kf, sf, acc[d]);
+            } else {
+              acc[d] = mma<T>(Tile::tr_frag(Ks, 2 * kb + kk, 32 * d, lane), sf, acc[d]);
+            }
+          }
         }
         if constexpr (sizeof(T) == 2) {
           // the transposed K fragments of product n + 1 are read before product n
