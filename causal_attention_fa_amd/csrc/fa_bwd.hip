@@ -172,19 +172,22 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
   // and kept in registers so a read's tile and step parts are its immediate:
   // fro: row r, columns 16t + 8h of a 32-row Q / dO block; vro: the same in
   // this wave's V rows; tro: the two transposed reads for dK / dV columns 32d
+  // (with two groups the group's buffer pair is part of fro and tro, so the
+  // buffer of a step is a compile-time constant)
   uint32_t fro[HD / 16], vro[HD / 16], tro[HD / 32][2];
   if constexpr (sizeof(T) == 2) {
+    const uint32_t gb = NG == 1 ? 0u : (uint32_t)(grp * 2 * kElems * (int)sizeof(T));
 #pragma unroll
     for (int t = 0; t < HD / 16; ++t) {
-      fro[t] = (uint32_t)(Tile::at(r, 16 * t + 8 * h) * (int)sizeof(T));
+      fro[t] = gb + (uint32_t)(Tile::at(r, 16 * t + 8 * h) * (int)sizeof(T));
       vro[t] = (uint32_t)(VTile::at(32 * w + r, 16 * t + 8 * h) * (int)sizeof(T));
     }
     const int x = 4 * (lane >> 5) + ((lane & 15) >> 2);
 #pragma unroll
     for (int d = 0; d < HD / 32; ++d) {
       const int col = 32 * d + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      tro[d][0] = (uint32_t)(Tile::at(x, col) * (int)sizeof(T));
-      tro[d][1] = (uint32_t)(Tile::at(x + 8, col) * (int)sizeof(T));
+      tro[d][0] = gb + (uint32_t)(Tile::at(x, col) * (int)sizeof(T));
+      tro[d][1] = gb + (uint32_t)(Tile::at(x + 8, col) * (int)sizeof(T));
     }
   }
 
@@ -268,6 +271,9 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     auto at_b = [](const T* base, uint32_t b) __attribute__((always_inline)) {
       return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + b);
     };
+    // the step's buffer pair of group 0 (the group's offset is in fro and tro)
+    const T* Qb = lds + buf * kElems + kOffQ;
+    const T* dOb = lds + buf * kElems + kOffD;
     // does a query of the tile see one of this wave's keys?  (a group with
     // one iteration fewer sits out the last step)
     const bool active = it < mine && (!CAUSAL || i0 + BQ - 1 + off >= kw0) &&
@@ -297,8 +303,8 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
           constexpr int LA = AHEAD ? 2 : 1;
           vec8<T> qq[NS], oq[NS], vq[NS];
           auto rd = [&](int t) __attribute__((always_inline)) {
-            qq[t] = load8<T>(at_b(Qs + 32 * qb * Tile::kStride, fro[t]));
-            oq[t] = load8<T>(at_b(dOs + 32 * qb * Tile::kStride, fro[t]));
+            qq[t] = load8<T>(at_b(Qb + 32 * qb * Tile::kStride, fro[t]));
+            oq[t] = load8<T>(at_b(dOb + 32 * qb * Tile::kStride, fro[t]));
             vq[t] = load8<T>(at_b(lds_v, vro[t]));
           };
           rd(0);
@@ -391,8 +397,8 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
               const vec4<T> a4 = lds_tr4<T>(at_b(tb, tro[d][0])), b4 = lds_tr4<T>(at_b(tb, tro[d][1]));
               return vec8<T>{a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]};
             };
-            dv[d] = mma<T>(trp(dOs), pf, dv[d]);
-            dk[d] = mma<T>(trp(Qs), sf, dk[d]);
+            dv[d] = mma<T>(trp(dOb), pf, dv[d]);
+            dk[d] = mma<T>(trp(Qb), sf, dk[d]);
           } else {
             dv[d] = mma<T>(Tile::tr_frag(dOs, kt, 32 * d, lane), pf, dv[d]);
             dk[d] = mma<T>(Tile::tr_frag(Qs, kt, 32 * d, lane), sf, dk[d]);
