@@ -32,11 +32,12 @@
 //   (XOR-swizzled, direct global->LDS loads) in LDS (A operands of S and dP);
 //   the A operands of the gradient products,
 //   dO^T and Q^T, come from gfx950's LDS transpose read of the same tiles.  L
-//   and D of the tile's rows are staged in LDS too.  The kernel fits two waves
-//   per SIMD only with each transpose read waited for right before its
-//   product.  Small grids take one of two variants: two wave groups sharing
-//   a workgroup's keys (one workgroup per CU or fewer), or reading the next
-//   product's fragments ahead at one wave per SIMD (up to three per CU).
+//   and D of the tile's rows are staged in LDS too.  Each transpose read is
+//   issued one product ahead; this fits two waves per SIMD because the
+//   per-lane read offsets are computed once and kept in registers.  Small
+//   grids take one of two variants: two wave groups sharing a workgroup's keys
+//   (one workgroup per CU or fewer), or one wave per SIMD with the S and dP
+//   fragments read two steps ahead (up to three per CU).
 //   dq: S^T = K Q^T and dP^T = V dO^T put one query row per lane pair (like
 //   the forward), and dS^T is the B operand of dQ^T += K^T dS^T, whose K^T
 //   operand is a transpose read of the row-major K tile.
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
 
   // keys past the end read key skv-1: their dK, dV are never stored.  K stays
   // in registers (B operand of S); V, the B operand of dP, is read from LDS
-  // each tile, which keeps the kernel within 256 VGPRs (two workgroups per CU)
+  // each tile, which keeps the kernel within 256 VGPRs (two waves per SIMD)
   vec8<T> kf[HD / 16];
   {
     const size_t o = (size_t)min(mykv, sv0.skv - 1) * HD + 8 * h;
@@ -168,20 +169,23 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     dk[d] = f32x16{};
     dv[d] = f32x16{};
   }
-  // byte offsets of the lane's fragment reads (16-bit tiles), computed once
-  // and kept in registers so a read's tile and step parts are its immediate:
-  // fro: row r, columns 16t + 8h of a 32-row Q / dO block; vro: the same in
-  // this wave's V rows; tro: the two transposed reads for dK / dV columns 32d
-  // (with two groups the group's buffer pair is part of fro and tro, so the
-  // buffer of a step is a compile-time constant)
-  uint32_t fro[HD / 16], vro[HD / 16], tro[HD / 32][2];
-  if constexpr (sizeof(T) == 2) {
+  // byte offsets of the lane's Q / dO fragment reads (16-bit tiles), computed
+  // once and kept in registers so a read's tile and step parts are its
+  // immediate (the compiler otherwise recomputed the swizzled addresses every
+  // tile): fro: row r, columns 16t + 8h of a 32-row block; tro: the two
+  // transposed reads for dK / dV columns 32d.  With two groups the group's
+  // buffer pair is part of them, so the buffer of a step is a compile-time
+  // constant.  The registers this frees let the gradient products read their
+  // transposed fragments one product ahead at two waves per SIMD.
+  // (The one-group 4-wave bias kernel at D = 128 keeps computing its
+  // addresses, with its buffer chosen at run time: held offsets or the
+  // unrolled loop take it past 256 registers, which halves its waves per SIMD.)
+  constexpr bool kPin = sizeof(T) == 2 && !(ALIBI && NG == 1 && NW == 4 && !AHEAD && HD == 128);
+  uint32_t fro[HD / 16], tro[HD / 32][2];
+  if constexpr (kPin) {
     const uint32_t gb = NG == 1 ? 0u : (uint32_t)(grp * 2 * kElems * (int)sizeof(T));
 #pragma unroll
-    for (int t = 0; t < HD / 16; ++t) {
-      fro[t] = gb + (uint32_t)(Tile::at(r, 16 * t + 8 * h) * (int)sizeof(T));
-      vro[t] = (uint32_t)(VTile::at(32 * w + r, 16 * t + 8 * h) * (int)sizeof(T));
-    }
+    for (int t = 0; t < HD / 16; ++t) fro[t] = gb + (uint32_t)(Tile::at(r, 16 * t + 8 * h) * (int)sizeof(T));
     const int x = 4 * (lane >> 5) + ((lane & 15) >> 2);
 #pragma unroll
     for (int d = 0; d < HD / 32; ++d) {
@@ -251,8 +255,9 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
   }
   __syncthreads();
   // unrolled by two: every LDS address names its buffer at compile time
+  // (except in the kernel that keeps computing its addresses, see kPin)
   auto body = [&](const int it, auto bufc) __attribute__((always_inline)) {
-    constexpr int buf = decltype(bufc)::value;
+    const int buf = bufc;
     const int i0 = cur_qt * BQ;
     const bool more = it + 1 < mine;
     if (more) {  // the other buffer was last read before the previous barrier
@@ -262,9 +267,9 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     }
     const T* Qs = lds + (grp * 2 + buf) * kElems + kOffQ;
     const T* dOs = lds + (grp * 2 + buf) * kElems + kOffD;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (kPin) {
 #pragma unroll
-      for (int t = 0; t < HD / 16; ++t) asm volatile("" : "+v"(fro[t]), "+v"(vro[t]));
+      for (int t = 0; t < HD / 16; ++t) asm volatile("" : "+v"(fro[t]));
 #pragma unroll
       for (int d = 0; d < HD / 32; ++d) asm volatile("" : "+v"(tro[d][0]), "+v"(tro[d][1]));
     }
@@ -298,20 +303,27 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
           // the Q, dO and V fragments of step t + LA are read before the
           // products of step t, in registers of their own, and a fence after
           // every step keeps the S and dP products alternating; the read-ahead
-          // variant (one wave per SIMD) has the registers for two steps
+          // variant (one wave per SIMD) has the registers for two steps, the
+          // bias kernel that computes its addresses (kPin) for none
           constexpr int NS = HD / 16;
-          constexpr int LA = AHEAD ? 2 : 1;
+          constexpr int LA = AHEAD ? 2 : kPin ? 1 : 0;
           vec8<T> qq[NS], oq[NS], vq[NS];
           auto rd = [&](int t) __attribute__((always_inline)) {
-            qq[t] = load8<T>(at_b(Qb + 32 * qb * Tile::kStride, fro[t]));
-            oq[t] = load8<T>(at_b(dOb + 32 * qb * Tile::kStride, fro[t]));
-            vq[t] = load8<T>(at_b(lds_v, vro[t]));
+            if constexpr (kPin) {
+              qq[t] = load8<T>(at_b(Qb + 32 * qb * Tile::kStride, fro[t]));
+              oq[t] = load8<T>(at_b(dOb + 32 * qb * Tile::kStride, fro[t]));
+            } else {
+              qq[t] = Tile::frag(Qs, 32 * qb + r, 16 * t, h);
+              oq[t] = Tile::frag(dOs, 32 * qb + r, 16 * t, h);
+            }
+            vq[t] = VTile::frag(lds_v, 32 * w + r, 16 * t, h);
           };
-          rd(0);
+          if constexpr (LA > 0) rd(0);
           if constexpr (LA == 2) rd(1);
 #pragma unroll
           for (int t = 0; t < NS; ++t) {
-            if (t + LA < NS) rd(t + LA);
+            if constexpr (LA == 0) rd(t);
+            if (LA > 0 && t + LA < NS) rd(t + LA);
             s[qb] = mma<T>(qq[t], kf[t], t == 0 ? f32x16{} : s[qb]);
             dp[qb] = mma<T>(oq[t], vq[t], t == 0 ? nd : dp[qb]);
             __builtin_amdgcn_sched_barrier(0);
@@ -391,7 +403,7 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
         const vec8<T> sf = acc_to_frag<T>(dp[kt >> 1], 8 * (kt & 1));
 #pragma unroll
         for (int d = 0; d < HD / 32; ++d) {
-          if constexpr (sizeof(T) == 2) {
+          if constexpr (kPin) {
             auto trp = [&](const T* tile) __attribute__((always_inline)) {
               const T* tb = tile + 16 * kt * Tile::kStride;
               const vec4<T> a4 = lds_tr4<T>(at_b(tb, tro[d][0])), b4 = lds_tr4<T>(at_b(tb, tro[d][1]));
@@ -405,9 +417,10 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
           }
         }
       }
-      if constexpr (AHEAD && sizeof(T) == 2) {
+      if constexpr ((AHEAD || NW == 8 || NG == 2 || HD == 64) && sizeof(T) == 2) {
         // the transposed fragments of product n + 1 are read before product n
-        // (needs more than 256 registers: one wave per SIMD)
+        // (the one-group 4-wave form at D = 128, used with the bias, would need
+        // more than 256 registers for it)
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
 #pragma unroll
         for (int n = 0; n < 2 * (BQ / 16) * (HD / 32) - 1; ++n) {
@@ -422,9 +435,13 @@ __global__ __launch_bounds__(NG * NW * 64, 1) void dkdv_kernel(
     for (int k = 0; k < NG; ++k) advance(cur_hq, cur_qt);
     __syncthreads();
   };
-  for (int it = 0; it < steps; it += 2) {
-    body(it, std::integral_constant<int, 0>{});
-    if (it + 1 < steps) body(it + 1, std::integral_constant<int, 1>{});
+  if constexpr (kPin || sizeof(T) == 4) {
+    for (int it = 0; it < steps; it += 2) {
+      body(it, std::integral_constant<int, 0>{});
+      if (it + 1 < steps) body(it + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    for (int it = 0; it < steps; ++it) body(it, it & 1);
   }
 
   if constexpr (NG == 2) {

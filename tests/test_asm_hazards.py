@@ -147,3 +147,28 @@ def test_no_kernel_spills(kernel_asm, src):
     assert sizes, "no kernel descriptors found"
     spilling = [(k, int(n)) for k, n in sizes if int(n) != 0]
     assert not spilling, f"{src}: kernels using scratch memory: {spilling[:3]}"
+
+
+def _two_wave_kernels(asm):
+    """(name, registers) of the 16-bit gradient kernels meant to run two waves per
+    SIMD: every dQ and dK/dV instance except the dK/dV read-ahead form, which runs
+    one wave per SIMD by design.  `.amdhsa_next_free_vgpr` counts the vector and
+    accumulation registers together; above 256 a SIMD holds only one such wave."""
+    out = []
+    for name, n in re.findall(r"\.amdhsa_kernel (\S+)[\s\S]*?\.amdhsa_next_free_vgpr (\d+)", asm):
+        if not ("DF16_" in name or "DF16b" in name):
+            continue
+        if "dq_kernel" in name:
+            out.append((name, int(n)))
+        elif "dkdv_kernel" in name:
+            flags = re.findall(r"ELb([01])", name)
+            if len(flags) == 4 and flags[3] == "0":
+                out.append((name, int(n)))
+    return out
+
+
+def test_two_wave_gradient_kernels_fit_256_registers(kernel_asm):
+    found = _two_wave_kernels(kernel_asm["fa_bwd.hip"])
+    assert len(found) >= 40, f"only {len(found)} gradient kernels found: the check would prove little"
+    over = [(k, n) for k, n in found if n > 256]
+    assert not over, f"kernels past 256 registers (one wave per SIMD): {over[:3]}"
