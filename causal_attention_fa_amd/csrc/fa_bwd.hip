@@ -37,7 +37,8 @@
 //   per-lane read offsets are computed once and kept in registers.  Small
 //   grids take one of two variants: two wave groups sharing a workgroup's keys
 //   (one workgroup per CU or fewer), or one wave per SIMD with the S and dP
-//   fragments read two steps ahead (up to three per CU).
+//   fragments read two steps ahead (up to two per CU at D = 128, where the
+//   8-wave kernel takes larger grids; up to three otherwise).
 //   dq: S^T = K Q^T and dP^T = V dO^T put one query row per lane pair (like
 //   the forward), and dS^T is the B operand of dQ^T += K^T dS^T, whose K^T
 //   operand is a transpose read of the row-major K tile.
@@ -809,7 +810,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     //   up to one workgroup per CU: two wave groups per workgroup (+35 % at
     //     S = 4096 with 32/8 heads; ALiBi's extra registers do not fit it);
     //   up to three: the read-ahead variant, one wave per SIMD (+13 % at one
-    //     workgroup per CU, +2 % at three; at four it loses 9 %).
+    //     workgroup per CU, +2 % at three; at four it loses 9 %); where the
+    //     8-wave kernel below exists, up to two only (against it: +15 % at
+    //     S = 8192, +20 % at 6144; above two it wins, +1.5 % at S = 10240 and
+    //     +10.6 % at 12288, 32/8 heads).
     // Larger 16-bit D = 128 grids: 8-wave workgroups of 256 keys (one per CU),
     // so that each Q / dO tile a workgroup loads serves twice the keys and the
     // L2 reads of those tiles halve (+1.1 % on the long-context backward).
@@ -822,7 +826,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
             done = true;
           }
         }
-        if (!done && (long long)grid.x <= 3 * kCUs) {
+        constexpr bool kHas8 = HD == 128 && !ALIBI;  // the 8-wave kernel below
+        if (!done && (long long)grid.x <= (kHas8 ? 2 : 3) * kCUs) {
           launch_dkdv<T, HD, BQ, NW, 1, CAUSAL, WINDOW, ALIBI, true>(a, st, grid, c, nkt);
           done = true;
         }

@@ -282,7 +282,7 @@ def test_wide_grid_masks(causal, window, S, Skv, D, dtype):
 @pytest.mark.parametrize("causal,window,S", [(True, None, 2048), (True, None, 1999), (False, 600, 2048)])
 def test_read_ahead_dkdv_grid(causal, window, S, dtype):
     """B = 4, 32/8 heads, D = 128: ceil(S/128) * 4 * 8 = 512 four-wave key blocks, more
-    than one and at most three per CU, which dispatches the dK/dV kernel's one-wave-per-SIMD
+    than one and at most two per CU, which dispatches the dK/dV kernel's one-wave-per-SIMD
     form that reads its fragments ahead (and, with 8-wave query blocks from 256, the
     8-wave forward).  One whole KV group's O and gradients against the oracle, and
     sampled rows of the gradients of every other KV head (and the last)."""
