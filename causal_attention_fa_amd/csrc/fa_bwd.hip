@@ -36,9 +36,9 @@
 //   issued one product ahead; this fits two waves per SIMD because the
 //   per-lane read offsets are computed once and kept in registers.  Small
 //   grids take one of two variants: two wave groups sharing a workgroup's keys
-//   (one workgroup per CU or fewer), or one wave per SIMD with the S and dP
-//   fragments read two steps ahead (up to two per CU at D = 128, where the
-//   8-wave kernel takes larger grids; up to three otherwise).
+//   (up to three workgroups per CU at D = 128, two at D = 64), or one wave per
+//   SIMD with the S and dP fragments read two steps ahead (D = 64 up to three
+//   per CU, and the bias kernels, which two groups do not fit).
 //   dq: S^T = K Q^T and dP^T = V dO^T put one query row per lane pair (like
 //   the forward), and dS^T is the B operand of dQ^T += K^T dS^T, whose K^T
 //   operand is a transpose read of the row-major K tile.
@@ -806,14 +806,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int nkt = (pb.Skv + 32 * NW - 1) / (32 * NW);
     dim3 grid(nkt * pb.B * pb.Hkv);
     mark(a.ev, a.nev, 1, st);
-    // Small grids (measured on the backward, against the plain kernel):
-    //   up to one workgroup per CU: two wave groups per workgroup (+35 % at
-    //     S = 4096 with 32/8 heads; ALiBi's extra registers do not fit it);
-    //   up to three: the read-ahead variant, one wave per SIMD (+13 % at one
-    //     workgroup per CU, +2 % at three; at four it loses 9 %); where the
-    //     8-wave kernel below exists, up to two only (against it: +15 % at
-    //     S = 8192, +20 % at 6144; above two it wins, +1.5 % at S = 10240 and
-    //     +10.6 % at 12288, 32/8 heads).
+    // Grids counted in 4-wave workgroups of 128 keys (measured on the backward):
+    //   two wave groups per workgroup up to three per CU at D = 128 (against
+    //     the next choice: +16 % at S = 6144, +11 % at 8192, +15 % at 10240,
+    //     +7 % at 12288 with 32/8 heads, a tie at 16384) and up to two at
+    //     D = 64 (+14 % at two, mixed at three); ALiBi's extra registers do
+    //     not fit it;
+    //   then up to three: the read-ahead variant, one wave per SIMD (+13 % at
+    //     one workgroup per CU, +2 % at three against the plain kernel; at
+    //     four it loses 9 %).
     // Larger 16-bit D = 128 grids: 8-wave workgroups of 256 keys (one per CU),
     // so that each Q / dO tile a workgroup loads serves twice the keys and the
     // L2 reads of those tiles halve (+1.1 % on the long-context backward).
@@ -821,13 +822,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       bool done = false;
       if constexpr (sizeof(T) == 2) {
         if constexpr (!ALIBI) {
-          if ((long long)grid.x <= kCUs) {
+          if ((long long)grid.x <= (HD == 128 ? 3 : 2) * kCUs) {
             launch_dkdv<T, HD, BQ, NW, 2, CAUSAL, WINDOW, ALIBI, false>(a, st, grid, c, nkt);
             done = true;
           }
         }
-        constexpr bool kHas8 = HD == 128 && !ALIBI;  // the 8-wave kernel below
-        if (!done && (long long)grid.x <= (kHas8 ? 2 : 3) * kCUs) {
+        if (!done && (long long)grid.x <= 3 * kCUs) {
           launch_dkdv<T, HD, BQ, NW, 1, CAUSAL, WINDOW, ALIBI, true>(a, st, grid, c, nkt);
           done = true;
         }
